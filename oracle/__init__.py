@@ -1,0 +1,13 @@
+"""FP64 CPU oracle (test infrastructure only; see ``oracle.attention``).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The HIP library and its Python binding
+never do, and this package never imports them.
+"""
+from .attention import (default_scale, attention, attention_head, int8_scores,
+                        attention_int8, attention_int8_head, quantize_int8,
+                        deviation, attention_probabilities, run_heads)
+
+__all__ = ["default_scale", "attention", "attention_head", "int8_scores",
+           "attention_int8", "attention_int8_head", "quantize_int8",
+           "deviation", "attention_probabilities", "run_heads"]

@@ -1,0 +1,340 @@
+"""Pins of the FP64 oracle to things other than itself.
+
+Each ``check_*`` takes a module that exposes the oracle's API and raises
+AssertionError when the module disagrees with what the mathematics fixes:
+a high-precision brute force written differently (no max shift, decimal
+arithmetic), a library routine (torch's float64 scaled-dot-product attention
+on the CPU), closed forms and invariants of softmax attention, and exact
+integer arithmetic for the int8 path.  ``test_oracle.py`` runs them on the
+oracle; ``test_oracle_mutants.py`` runs them on copies of the oracle with one
+planted mistake each and requires every copy to fail at least one of them.
+"""
+from __future__ import annotations
+
+import math
+from decimal import Decimal, getcontext
+
+import numpy as np
+
+PINS = []
+
+
+def pin(fn):
+    PINS.append(fn)
+    return fn
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+# ---------------------------------------------------------------------------
+# brute force: scalar decimal arithmetic, softmax without a max shift
+# ---------------------------------------------------------------------------
+
+def brute_force_attention(q, k, v, causal, scale):
+    """sum_j exp(s_ij) v_j / sum_j exp(s_ij) at 50 significant digits."""
+    getcontext().prec = 50
+    n, d = q.shape
+    dv = v.shape[1]
+    sc = Decimal(scale)
+    out = np.zeros((n, dv))
+    lse = np.zeros(n)
+    for i in range(n):
+        num = [Decimal(0)] * dv
+        den = Decimal(0)
+        for j in range(k.shape[0]):
+            if causal and j > i:
+                continue
+            dot = sum((Decimal(float(q[i, t])) * Decimal(float(k[j, t])) for t in range(d)),
+                      Decimal(0))
+            w = (sc * dot).exp()
+            den += w
+            for c in range(dv):
+                num[c] += w * Decimal(float(v[j, c]))
+        for c in range(dv):
+            out[i, c] = float(num[c] / den)
+        lse[i] = float(den.ln())
+    return out, lse
+
+
+@pin
+def check_brute_force(ora):
+    for seed, (n, d, dv, causal) in enumerate([(1, 3, 2, False), (5, 4, 3, True),
+                                               (6, 3, 5, False), (7, 2, 2, True)]):
+        rng = _rng(100 + seed)
+        q = rng.standard_normal((n, d)) * 1.7
+        k = rng.standard_normal((n, d)) * 1.3
+        v = rng.standard_normal((n, dv))
+        scale = 1.0 / math.sqrt(d)
+        o, lse = ora.attention(q, k, v, causal=causal, scale=scale, block_rows=3)
+        ob, lb = brute_force_attention(q, k, v, causal, scale)
+        assert np.allclose(o, ob, rtol=0, atol=1e-13), np.abs(o - ob).max()
+        assert np.allclose(lse, lb, rtol=0, atol=1e-13), np.abs(lse - lb).max()
+
+
+# ---------------------------------------------------------------------------
+# library routine: torch float64 SDPA on the CPU
+# ---------------------------------------------------------------------------
+
+@pin
+def check_torch_sdpa(ora):
+    import torch
+    import torch.nn.functional as F
+    rng = _rng(7)
+    for causal in (False, True):
+        for (b, h, n, d, block) in [(2, 3, 37, 16, 8), (1, 2, 130, 64, 64)]:
+            q = rng.standard_normal((b, h, n, d))
+            k = rng.standard_normal((b, h, n, d))
+            v = rng.standard_normal((b, h, n, d))
+            o, _ = ora.attention(q, k, v, causal=causal, block_rows=block)
+            ref = F.scaled_dot_product_attention(
+                torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v),
+                is_causal=causal, scale=1.0 / math.sqrt(d)).numpy()
+            assert np.allclose(o, ref, rtol=0, atol=1e-12), np.abs(o - ref).max()
+
+
+# ---------------------------------------------------------------------------
+# closed forms and invariants
+# ---------------------------------------------------------------------------
+
+@pin
+def check_default_scale(ora):
+    assert ora.default_scale(64) == 0.125
+    # 1/sqrt(128) = sqrt(2)/16
+    assert abs(ora.default_scale(128) - math.sqrt(2.0) / 16.0) <= 2.0 ** -56
+    assert ora.default_scale(1) == 1.0
+
+
+@pin
+def check_two_key_closed_form(ora):
+    """One query, two keys: O = sigma(s1 - s0) v1 + (1 - sigma) v0."""
+    for a in (-3.0, -0.25, 0.0, 0.7, 5.0):
+        q = np.array([[a, 0.0]])
+        k = np.array([[0.0, 1.0], [1.0, 1.0]])          # s0 = 0, s1 = a * scale
+        v = np.array([[2.0, -1.0], [-4.0, 3.0]])
+        scale = 1.0 / math.sqrt(2.0)
+        o, lse = ora.attention(q, k, v, causal=False, scale=scale)
+        w1 = 1.0 / (1.0 + math.exp(-a * scale))
+        expect = w1 * v[1] + (1.0 - w1) * v[0]
+        assert np.allclose(o[0], expect, rtol=0, atol=1e-15)
+        assert abs(lse[0] - math.log(1.0 + math.exp(a * scale))) < 1e-14
+
+
+@pin
+def check_zero_query_is_mean(ora):
+    """Q = 0 gives equal weights: the column mean of V, or of the causal prefix."""
+    rng = _rng(11)
+    n, d = 45, 8
+    q = np.zeros((n, d))
+    k = rng.standard_normal((n, d))
+    v = rng.standard_normal((n, d))
+    o, lse = ora.attention(q, k, v, causal=False, block_rows=16)
+    assert np.allclose(o, v.mean(axis=0)[None, :], rtol=0, atol=1e-14)
+    assert np.allclose(lse, math.log(n), rtol=0, atol=1e-14)
+    o, lse = ora.attention(q, k, v, causal=True, block_rows=16)
+    prefix = np.cumsum(v, axis=0) / np.arange(1, n + 1)[:, None]
+    assert np.allclose(o, prefix, rtol=0, atol=1e-14)
+    assert np.allclose(lse, np.log(np.arange(1, n + 1)), rtol=0, atol=1e-14)
+
+
+@pin
+def check_key_value_permutation(ora):
+    """Non-causal attention is invariant to permuting keys with their values."""
+    rng = _rng(12)
+    n, d = 50, 8
+    q, k, v = (rng.standard_normal((n, d)) for _ in range(3))
+    perm = rng.permutation(n)
+    o1, l1 = ora.attention(q, k, v, causal=False, block_rows=16)
+    o2, l2 = ora.attention(q, k[perm], v[perm], causal=False, block_rows=16)
+    assert np.allclose(o1, o2, rtol=0, atol=1e-13)
+    assert np.allclose(l1, l2, rtol=0, atol=1e-13)
+
+
+@pin
+def check_rows_of_p_sum_to_one(ora):
+    rng = _rng(13)
+    for causal in (False, True):
+        q, k = (rng.standard_normal((33, 5)) * 2 for _ in range(2))
+        p = ora.attention_probabilities(q, k, causal=causal, scale=0.6)
+        assert np.allclose(p.sum(axis=1), 1.0, rtol=0, atol=1e-14)
+        assert (p >= 0).all()
+        if causal:
+            assert (np.triu(p, 1) == 0).all()
+
+
+@pin
+def check_probabilities_drive_output(ora):
+    """O equals P V for the P the oracle reports (and P matches brute force)."""
+    rng = _rng(14)
+    q, k, v = (rng.standard_normal((9, 4)) for _ in range(3))
+    for causal in (False, True):
+        p = ora.attention_probabilities(q, k, causal=causal, scale=0.5)
+        o, _ = ora.attention(q, k, v, causal=causal, scale=0.5, block_rows=4)
+        assert np.allclose(o, p @ v, rtol=0, atol=1e-14)
+        ones = np.eye(9)
+        pb, _ = brute_force_attention(q, k, ones, causal, 0.5)
+        assert np.allclose(p, pb, rtol=0, atol=1e-14)
+
+
+@pin
+def check_causal_special_rows(ora):
+    """Causal row 0 sees only key 0 (O_0 = V_0); N = 1 gives O = V; a constant
+    V gives that constant; adding one vector to every key changes nothing."""
+    rng = _rng(15)
+    n, d = 40, 6
+    q, k, v = (rng.standard_normal((n, d)) for _ in range(3))
+    o, _ = ora.attention(q, k, v, causal=True, block_rows=8)
+    assert np.array_equal(o[0], v[0])
+    o1, _ = ora.attention(q[:1], k[:1], v[:1], causal=False)
+    assert np.allclose(o1, v[:1], rtol=0, atol=1e-15)
+    const = np.tile(rng.standard_normal((1, d)), (n, 1))
+    for causal in (False, True):
+        oc, _ = ora.attention(q, k, const, causal=causal, block_rows=8)
+        assert np.allclose(oc, const, rtol=0, atol=1e-14)
+        u = rng.standard_normal((1, d))
+        oa, la = ora.attention(q, k, v, causal=causal, block_rows=8)
+        ob, lb = ora.attention(q, k + u, v, causal=causal, block_rows=8)
+        assert np.allclose(oa, ob, rtol=0, atol=1e-12)
+        shift = (q @ u.T)[:, 0] / math.sqrt(d)
+        assert np.allclose(lb - la, shift, rtol=0, atol=1e-12)
+
+
+@pin
+def check_large_scores_hard_limit(ora):
+    """Huge scores must not overflow: the softmax tends to a hard argmax."""
+    rng = _rng(16)
+    n, d = 24, 4
+    k = rng.standard_normal((n, d))
+    v = rng.standard_normal((n, d))
+    q = 4000.0 * k[[5, 17, 3]]                 # each query aligns with one key
+    o, lse = ora.attention(q, k, v, causal=False, scale=1.0, block_rows=2)
+    s = q @ k.T
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    assert np.allclose(o, v[np.argmax(s, axis=1)], rtol=0, atol=1e-12)
+    assert np.allclose(lse, s.max(axis=1), rtol=1e-15, atol=0)
+    q2 = np.concatenate([q, -q])              # row maxima of very different size
+    p = ora.attention_probabilities(q2, k, causal=False, scale=1.0)
+    s2 = q2 @ k.T
+    assert np.all(np.isfinite(p))
+    assert np.array_equal(np.argmax(p, axis=1), np.argmax(s2, axis=1))
+    assert np.allclose(p.max(axis=1), 1.0, rtol=0, atol=1e-12)
+
+
+@pin
+def check_blocking_is_invisible(ora):
+    """The row-block size is a memory measure only: results agree to rounding."""
+    rng = _rng(17)
+    q, k, v = (rng.standard_normal((2, 2, 70, 8)) for _ in range(3))
+    for causal in (False, True):
+        ref, lref = ora.attention(q, k, v, causal=causal, block_rows=70)
+        for br in (1, 3, 16, 64):
+            o, l = ora.attention(q, k, v, causal=causal, block_rows=br)
+            assert np.allclose(o, ref, rtol=0, atol=1e-14)
+            assert np.allclose(l, lref, rtol=0, atol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# int8 path
+# ---------------------------------------------------------------------------
+
+@pin
+def check_int8_scores_exact(ora):
+    """D equals the Python-integer dot products, including the extremes."""
+    rng = _rng(18)
+    qc = rng.integers(-127, 128, size=(2, 11, 128), dtype=np.int64).astype(np.int8)
+    kc = rng.integers(-127, 128, size=(2, 13, 128), dtype=np.int64).astype(np.int8)
+    qc[0, 0, :] = 127
+    kc[0, 0, :] = 127
+    kc[0, 1, :] = -127
+    dots = ora.int8_scores(qc, kc)
+    assert dots.dtype == np.int64
+    for b in range(2):
+        for i in range(11):
+            for j in range(13):
+                exact = sum(int(x) * int(y) for x, y in zip(qc[b, i], kc[b, j]))
+                assert dots[b, i, j] == exact
+    assert dots[0, 0, 0] == 128 * 127 * 127
+    assert dots[0, 0, 1] == -128 * 127 * 127
+
+
+@pin
+def check_int8_attention_matches_dequantised(ora):
+    """int8 attention equals float attention on the dequantised rows
+    sq_i * code_i (the scores are scale * sq_i * sk_j * D_ij)."""
+    rng = _rng(19)
+    n, d = 21, 16
+    qc = rng.integers(-127, 128, size=(n, d)).astype(np.int8)
+    kc = rng.integers(-127, 128, size=(n, d)).astype(np.int8)
+    sq = rng.uniform(0.001, 0.03, size=n).astype(np.float32)
+    sk = rng.uniform(0.001, 0.03, size=n).astype(np.float32)
+    v = rng.standard_normal((n, d))
+    for causal in (False, True):
+        o, lse = ora.attention_int8(qc, sq, kc, sk, v, causal=causal, block_rows=5)
+        qd = qc.astype(np.float64) * sq.astype(np.float64)[:, None]
+        kd = kc.astype(np.float64) * sk.astype(np.float64)[:, None]
+        ob, lb = brute_force_attention(qd, kd, v, causal, 1.0 / math.sqrt(d))
+        assert np.allclose(o, ob, rtol=0, atol=1e-13)
+        assert np.allclose(lse, lb, rtol=0, atol=1e-13)
+
+
+@pin
+def check_quantiser(ora):
+    # a row whose absmax is 127 has scale exactly 1: codes are rint(x), with
+    # ties to even
+    row = np.array([[127.0, 0.5, 1.5, 2.5, -2.5, -0.5, 3.49, -126.5]], np.float32)
+    codes, scale = ora.quantize_int8(row)
+    assert scale.dtype == np.float32 and scale[0] == 1.0
+    assert codes.tolist() == [[127, 0, 2, 2, -2, 0, 3, -126]]
+    # absmax = 0 -> scale 1, codes 0
+    codes, scale = ora.quantize_int8(np.zeros((2, 8), np.float32))
+    assert (codes == 0).all() and (scale == 1.0).all()
+    # random rows: the absmax element maps to +-127, codes are odd-symmetric,
+    # and every code reconstructs its value within half a step
+    rng = _rng(20)
+    x = rng.standard_normal((64, 128)).astype(np.float32)
+    codes, scale = ora.quantize_int8(x)
+    c2, s2 = ora.quantize_int8(-x)
+    assert np.array_equal(c2, -codes) and np.array_equal(s2, scale)
+    am = np.abs(x).max(axis=1)
+    # fp64 quotient rounded once to fp32 is the correctly rounded fp32 quotient
+    # (53 >= 2*24 + 2), an independent route to the same scale
+    assert np.array_equal(scale, (am.astype(np.float64) / 127).astype(np.float32))
+    idx = np.abs(x).argmax(axis=1)
+    assert (np.abs(codes[np.arange(64), idx]) == 127).all()
+    err = np.abs(codes.astype(np.float64) * scale[:, None] - x.astype(np.float64))
+    assert (err <= scale[:, None].astype(np.float64) * (0.5 + 1e-5)).all()
+    assert codes.dtype == np.int8 and np.abs(codes.astype(int)).max() <= 127
+
+
+# ---------------------------------------------------------------------------
+# deviation summary
+# ---------------------------------------------------------------------------
+
+@pin
+def check_deviation(ora):
+    rng = _rng(21)
+    ref = rng.integers(-4096, 4096, size=1000) / 1024.0        # exact binary values
+    # a single spike
+    test = ref.copy()
+    test[417] += 0.25
+    st = ora.deviation(test, ref)
+    assert st["max_abs"] == 0.25 and st["argmax"] == 417
+    assert st["mean_abs"] == 0.25 / 1000 and st["mean_signed"] == 0.25 / 1000
+    assert abs(st["rms"] - math.sqrt(0.0625 / 1000)) < 1e-18
+    assert st["n"] == 1000 and st["n_nonfinite"] == 0
+    assert st["max_ref_abs"] == np.abs(ref).max()
+    assert st["rel_normwise"] == 0.25 / np.abs(ref).max()
+    # a constant negative offset: signed mean is the offset, mean |e| its size
+    st = ora.deviation(ref - 2.0 ** -10, ref)
+    assert st["mean_signed"] == -(2.0 ** -10) and st["mean_abs"] == 2.0 ** -10
+    assert st["max_abs"] == 2.0 ** -10 and st["argmax"] == 0
+    # ties in |e| report the first index; non-finite elements are counted
+    test = ref.copy()
+    test[[10, 20]] += 1.0
+    test[30] = np.nan
+    test[40] = np.inf
+    st = ora.deviation(test, ref)
+    assert st["argmax"] == 10 and st["max_abs"] == 1.0 and st["n_nonfinite"] == 2
+    assert st["mean_abs"] == 2.0 / 998
+    assert ora.deviation(ref, ref)["max_abs"] == 0.0

@@ -1,0 +1,92 @@
+"""Plant one mistake at a time in a copy of the oracle's source (on the CPU)
+and require the pins to catch every one.  This is what makes the pins worth
+trusting: a dropped term, a wrong sign, a wrong index or axis, or a transposed
+operand anywhere in the oracle fails at least one of them."""
+import os
+import types
+
+import pytest
+
+import oracle_pins
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                   "oracle", "attention.py")
+
+MUTANTS = [
+    ("diagonal dropped from causal mask", "return cols <= rows", "return cols < rows"),
+    ("causal mask reversed", "return cols <= rows", "return cols >= rows"),
+    ("scale dropped", "s = scale * (q[r0:r1] @ k[:kend].T)", "s = (q[r0:r1] @ k[:kend].T)"),
+    ("scale squared", "s = scale * (q[r0:r1] @ k[:kend].T)",
+     "s = scale * scale * (q[r0:r1] @ k[:kend].T)"),
+    ("keys in reverse order", "s = scale * (q[r0:r1] @ k[:kend].T)",
+     "s = scale * (q[r0:r1] @ k[:kend][::-1].T)"),
+    ("causal key range stops one short", "kend = r1 if causal else k.shape[0]",
+     "kend = r1 - 1 if causal and r1 > 1 else (r1 if causal else k.shape[0])"),
+    ("no max shift", "e = np.exp(s - m)", "e = np.exp(s)"),
+    ("max over the wrong axis", "m = s.max(axis=1, keepdims=True)",
+     "m = s.max(axis=0, keepdims=True)"),
+    ("row sum over the wrong axis", "ell = e.sum(axis=1, keepdims=True)",
+     "ell = e.sum(axis=0, keepdims=True)"),
+    ("no normalisation", "p = e / ell", "p = e"),
+    ("values shifted by one row", "o[r0:r1] = p @ v[:kend]",
+     "o[r0:r1] = p @ np.roll(v[:kend], 1, axis=0)"),
+    ("lse without log", "lse[r0:r1] = m[:, 0] + np.log(ell[:, 0])",
+     "lse[r0:r1] = m[:, 0] + ell[:, 0]"),
+    ("lse without max", "lse[r0:r1] = m[:, 0] + np.log(ell[:, 0])",
+     "lse[r0:r1] = np.log(ell[:, 0])"),
+    ("scale 1/d", "return 1.0 / math.sqrt(head_dim)", "return 1.0 / head_dim"),
+    ("P rows normalised over columns", "return w / w.sum(axis=1, keepdims=True)",
+     "return w / w.sum(axis=0, keepdims=True)"),
+    ("P without max shift", "w = np.exp(s - top)", "w = np.exp(s - top.mean())"),
+    ("int8 key scale dropped", "return scale * sq[r0:r1, None] * sk[None, :kend] * dots",
+     "return scale * sq[r0:r1, None] * dots"),
+    ("int8 scales swapped", "return scale * sq[r0:r1, None] * sk[None, :kend] * dots",
+     "return scale * sk[r0:r1, None] * sq[None, :kend] * dots"),
+    ("int8 scores transposed", "return np.rint(qf @ kt).astype(np.int64)",
+     "return np.rint(kf @ np.swapaxes(qf, -1, -2)).astype(np.int64)"),
+    ("quantiser truncates", "codes = np.clip(np.rint(ratio), -127.0, 127.0)",
+     "codes = np.clip(np.trunc(ratio), -127.0, 127.0)"),
+    ("quantiser rounds half away", "codes = np.clip(np.rint(ratio), -127.0, 127.0)",
+     "codes = np.clip(np.sign(ratio) * np.floor(np.abs(ratio) + 0.5), -127.0, 127.0)"),
+    ("quantiser divides by 128", "scale = (absmax / np.float32(127.0))",
+     "scale = (absmax / np.float32(128.0))"),
+    ("quantiser zero-row guard dropped",
+     "scale = np.where(scale == np.float32(0.0), np.float32(1.0), scale)",
+     "scale = np.where(scale == np.float32(0.0), np.float32(0.0), scale)"),
+    ("quantiser clamps at 128", "codes = np.clip(np.rint(ratio), -127.0, 127.0)",
+     "codes = np.clip(np.rint(ratio * np.float32(128.0 / 127.0)), -128.0, 127.0)"),
+    ("signed mean takes |e|", "mean_signed=float(ef.sum() / n_fin)",
+     "mean_signed=float(np.abs(ef).sum() / n_fin)"),
+    ("argmax reports the last tie", "arg = int(np.argmax(a))",
+     "arg = int(a.size - 1 - np.argmax(a[::-1]))"),
+    ("mean over all n", "mean_abs=float(np.abs(ef).sum() / n_fin)",
+     "mean_abs=float(np.abs(ef).sum() / n)"),
+    ("rms without root", "rms=float(math.sqrt((ef * ef).sum() / n_fin))",
+     "rms=float((ef * ef).sum() / n_fin)"),
+]
+
+
+def _mutant_module(old, new):
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation site not unique: {old!r}"
+    mod = types.ModuleType("oracle_mutant")
+    exec(compile(src.replace(old, new), SRC + " (mutant)", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_mutant(name, old, new):
+    mod = _mutant_module(old, new)
+    caught = []
+    for check in oracle_pins.PINS:
+        try:
+            check(mod)
+        except Exception as exc:               # AssertionError, or a crash
+            caught.append((check.__name__, type(exc).__name__))
+    assert caught, f"no pin catches mutant: {name}"
+
+
+def test_unmutated_copy_passes_all_pins():
+    mod = _mutant_module("def default_scale", "def default_scale")
+    for check in oracle_pins.PINS:
+        check(mod)
