@@ -1,0 +1,165 @@
+/*
+ * pnattn — exact softmax attention forward on AMD Instinct MI355X (gfx950).
+ *
+ * C ABI.  Plain C types only; every tensor is a pointer plus the sizes in an
+ * attn_problem_t.  No exception or C++ type crosses this boundary.
+ *
+ * The operation ("Why Low-Precision Transformer Training Fails", Algorithm 1,
+ * problem statement: Q, K, V in R^{N x d} split into row blocks of B_r and
+ * B_c rows; "Is Flash Attention Stable?", abstract: Flash versus Baseline
+ * Attention in an isolated forward pass at BF16):
+ *
+ *     S = scale * Q K^T   (causal: key j visible to query i iff j <= i)
+ *     O = softmax_rows(S) V
+ *
+ * for every (batch, head).  attn_fwd_flash never stores S (online softmax
+ * over key blocks); attn_fwd_baseline stores S and P in a workspace.
+ *
+ * Conventions shared by all entry points
+ *  - Layout: contiguous [batch][heads][seq_len][head_dim] ("BHSD"), head_dim
+ *    fastest; int8 scales are [batch][heads][seq_len].
+ *  - Pointers are device pointers (hipMalloc'd or torch CUDA tensors) unless
+ *    named *_host.  The caller owns every buffer; the library allocates no
+ *    device memory and keeps no state besides a thread-local error string.
+ *  - stream is a hipStream_t passed as void* (NULL = the default stream).
+ *    Calls enqueue work and return; kernel faults surface at the caller's
+ *    next synchronisation.  attn_deviation is the exception: it synchronises
+ *    its stream before it returns.
+ *  - Validation is pure host code and runs before any HIP call: on an error
+ *    nothing is launched and no output is touched.  attn_last_error() then
+ *    describes the failure.
+ */
+#ifndef PNATTN_H
+#define PNATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_INVALID_ARG = 1, /* null pointer, non-positive size, bad flag     */
+  ATTN_ERR_UNSUPPORTED = 2, /* valid but not built: head_dim, dtype combo    */
+  ATTN_ERR_WORKSPACE = 3,   /* workspace / scratch smaller than required     */
+  ATTN_ERR_HIP = 4          /* a HIP call failed; attn_last_error() has text */
+} attn_status_t;
+
+typedef enum {
+  ATTN_F32 = 0,  /* Q, K, V and O are fp32                                 */
+  ATTN_BF16 = 1, /* Q, K, V and O are bf16                                 */
+  ATTN_INT8 = 2  /* Q, K are int8 codes with fp32 per-row scales;
+                    V and O are bf16                                        */
+} attn_dtype_t;
+
+typedef struct {
+  int64_t batch;     /* >= 0 (0, like any zero size, is an empty problem:
+                        the call validates and returns ATTN_OK, launching
+                        nothing)                                            */
+  int64_t heads;     /* >= 0                                               */
+  int64_t seq_len;   /* N >= 0, at most 2^22; queries and keys have the
+                        same length                                         */
+  int64_t head_dim;  /* d: 64 or 128                                       */
+  int32_t causal;    /* 0 or 1 (key j visible to query i iff j <= i)       */
+  int32_t dtype;     /* attn_dtype_t                                       */
+  int32_t p_bf16;    /* 1: round the unnormalised probabilities P to bf16
+                        (round-to-nearest-even) before the P*V product,
+                        which then runs on bf16 MFMA; 0: keep P in fp32 and
+                        run P*V on fp32 MFMA (V widened exactly)            */
+  float softmax_scale; /* > 0; <= 0 selects 1/sqrt(head_dim)               */
+  int32_t stabilized;  /* reserved, must be 0                              */
+  float beta;          /* reserved, must be 0                              */
+} attn_problem_t;
+
+/* FlashAttention forward ("Why Low-Precision Transformer Training Fails",
+ * Algorithm 1, and the online-softmax accumulation that page's referee
+ * report places at its Eq. (2)):
+ * per query block, a running row max m, a running row sum l of the fp32
+ * unnormalised probabilities P = exp(S - m) (P is exactly 1 at the running
+ * row max, as that page's Figure 5 caption notes), and an exp-rescaled
+ * fp32 output accumulator; O = acc / l at the end.  S is never stored.
+ *   q, k   : [B,H,N,d] of dtype (int8 codes for ATTN_INT8)
+ *   v, o   : [B,H,N,d] fp32 for ATTN_F32, bf16 otherwise
+ *   q_scale, k_scale : [B,H,N] fp32, required for ATTN_INT8, else NULL
+ *   lse    : optional [B,H,N] fp32 log-sum-exp of each score row (natural
+ *            log, scaled scores), or NULL.                                 */
+attn_status_t attn_fwd_flash(const attn_problem_t* prob, const void* q,
+                             const void* k, const void* v,
+                             const float* q_scale, const float* k_scale,
+                             void* o, float* lse, void* stream);
+
+/* Debug form of the int8 flash kernel: the same kernel instance also writes
+ * each int32 score tile Qc Kc^T it computes (before scaling) to
+ * s_out [B,H,N,N] int32 (entries the kernel never computes, e.g. masked
+ * causal blocks, are left untouched).  ATTN_INT8 only; for checking that the
+ * integer products are exact ("INT-FlashAttention", abstract).           */
+attn_status_t attn_fwd_flash_debug_s(const attn_problem_t* prob, const void* q,
+                                     const void* k, const void* v,
+                                     const float* q_scale,
+                                     const float* k_scale, void* o,
+                                     int32_t* s_out, void* stream);
+
+/* Bytes of workspace attn_fwd_baseline needs: S [B,H,N,N] (fp32, or int32
+ * for ATTN_INT8) followed by P [B,H,N,N] (bf16 if p_bf16, else fp32).    */
+attn_status_t attn_baseline_workspace_size(const attn_problem_t* prob,
+                                           size_t* bytes);
+
+/* Baseline attention ("Is Flash Attention Stable?", abstract: the
+ * non-fused attention that Flash is compared with): three kernels on one
+ * stream.  K1 writes S = scale*QK^T (int32 Qc Kc^T for ATTN_INT8) for all
+ * N x N pairs; K2 applies the mask and a row softmax in fp32 and writes the
+ * normalised P (bf16 if p_bf16, else fp32); K3 computes O = P V with fp32
+ * accumulation.  workspace must hold attn_baseline_workspace_size bytes;
+ * S sits at offset 0 and can be read back after the call.                 */
+attn_status_t attn_fwd_baseline(const attn_problem_t* prob, const void* q,
+                                const void* k, const void* v,
+                                const float* q_scale, const float* k_scale,
+                                void* workspace, size_t workspace_bytes,
+                                void* o, void* stream);
+
+/* Summary of e = o_test - o_ref over n elements, the deviation of a
+ * low-precision forward output from a high-precision one ("Is Flash
+ * Attention Stable?", abstract; O_lp and O_hp in "Why Low-Precision
+ * Transformer Training Fails", Figure 5).  Elements with a non-finite e are
+ * counted in n_nonfinite and excluded from the other statistics; argmax is
+ * the first flat index of the largest |e| (-1 if none is finite).  Two-pass
+ * fixed-order reduction: the result is bitwise reproducible.             */
+typedef struct {
+  double max_abs, mean_abs, mean_signed, rms, max_ref_abs, rel_normwise;
+  int64_t n, n_nonfinite, argmax;
+} attn_deviation_t;
+
+/* Bytes of device scratch attn_deviation needs for n elements (n >= 0).  */
+attn_status_t attn_deviation_scratch_size(int64_t n, size_t* bytes);
+
+/*   o_test  : n elements of o_dtype (ATTN_F32 or ATTN_BF16)
+ *   o_ref   : n fp64 elements
+ *   n == 0 gives n = 0, argmax = -1 and zero statistics without a launch.
+ *   out_host: host pointer, filled after the stream has synchronised.     */
+attn_status_t attn_deviation(const void* o_test, int32_t o_dtype,
+                             const double* o_ref, int64_t n, void* scratch,
+                             size_t scratch_bytes, attn_deviation_t* out_host,
+                             void* stream);
+
+/* Symmetric per-row int8 quantisation of fp32 rows x [rows][d] (the int8
+ * Q/K input of "INT-FlashAttention", abstract; the per-row absmax/127
+ * granularity is this library's reading):
+ *   scale_r = fp32(absmax_r / 127)  (IEEE division), 1 if that is 0;
+ *   code    = clamp(round_half_even(fp32(x / scale_r)), -127, 127).
+ * codes: [rows][d] int8, scales: [rows] fp32.  1 <= d <= 1024.            */
+attn_status_t attn_quantize_int8(const float* x, int64_t rows, int64_t d,
+                                 int8_t* codes, float* scales, void* stream);
+
+const char* attn_status_string(attn_status_t status);
+/* Detail of the last failing call on this thread ("" if none).           */
+const char* attn_last_error(void);
+/* Library version string.                                                 */
+const char* attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PNATTN_H */

@@ -1,0 +1,250 @@
+"""ctypes binding of libpnattn (argument marshalling only).
+
+Each function has the name of the C entry point it calls.  Tensors are torch
+CUDA tensors (contiguous, BHSD); they supply device pointers and the stream
+(torch's current stream unless one is given).  Every step of the attention
+computation runs in the library's HIP kernels: there is no host fallback, and
+a missing library raises at load time.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libpnattn.so")
+
+ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE, ATTN_ERR_HIP = range(5)
+ATTN_F32, ATTN_BF16, ATTN_INT8 = 0, 1, 2
+
+
+class AttnProblem(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int64),
+        ("heads", ctypes.c_int64),
+        ("seq_len", ctypes.c_int64),
+        ("head_dim", ctypes.c_int64),
+        ("causal", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("p_bf16", ctypes.c_int32),
+        ("softmax_scale", ctypes.c_float),
+        ("stabilized", ctypes.c_int32),
+        ("beta", ctypes.c_float),
+    ]
+
+
+class AttnDeviation(ctypes.Structure):
+    _fields_ = [
+        ("max_abs", ctypes.c_double),
+        ("mean_abs", ctypes.c_double),
+        ("mean_signed", ctypes.c_double),
+        ("rms", ctypes.c_double),
+        ("max_ref_abs", ctypes.c_double),
+        ("rel_normwise", ctypes.c_double),
+        ("n", ctypes.c_int64),
+        ("n_nonfinite", ctypes.c_int64),
+        ("argmax", ctypes.c_int64),
+    ]
+
+    def as_dict(self) -> dict:
+        return {name: getattr(self, name) for name, _ in self._fields_}
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{message} (status {status})")
+        self.status = status
+
+
+_P = ctypes.c_void_p
+_SIGNATURES = {
+    "attn_fwd_flash": [ctypes.POINTER(AttnProblem), _P, _P, _P, _P, _P, _P, _P, _P],
+    "attn_fwd_flash_debug_s": [ctypes.POINTER(AttnProblem), _P, _P, _P, _P, _P, _P, _P, _P],
+    "attn_baseline_workspace_size": [ctypes.POINTER(AttnProblem), ctypes.POINTER(ctypes.c_size_t)],
+    "attn_fwd_baseline": [ctypes.POINTER(AttnProblem), _P, _P, _P, _P, _P, _P, ctypes.c_size_t,
+                          _P, _P],
+    "attn_deviation_scratch_size": [ctypes.c_int64, ctypes.POINTER(ctypes.c_size_t)],
+    "attn_deviation": [_P, ctypes.c_int32, _P, ctypes.c_int64, _P, ctypes.c_size_t,
+                       ctypes.POINTER(AttnDeviation), _P],
+    "attn_quantize_int8": [_P, ctypes.c_int64, ctypes.c_int64, _P, _P, _P],
+    "attn_status_string": [ctypes.c_int],
+    "attn_last_error": [],
+    "attn_version": [],
+}
+
+_LIB = None
+
+
+def load(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load libpnattn.so (built by ``precision_numerics_amd.build``)."""
+    global _LIB
+    if _LIB is not None and path is None:
+        return _LIB
+    path = path or LIB_PATH
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built: run `python -m precision_numerics_amd.build` "
+                           "(or __graft_entry__.build()) first; there is no fallback path")
+    lib = ctypes.CDLL(path)
+    for name, argtypes in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.argtypes = argtypes
+        fn.restype = ctypes.c_char_p if name in ("attn_status_string", "attn_last_error",
+                                                 "attn_version") else ctypes.c_int
+    if path == LIB_PATH:
+        _LIB = lib
+    return lib
+
+
+def _check(status: int):
+    if status != ATTN_OK:
+        lib = load()
+        msg = lib.attn_last_error().decode() or lib.attn_status_string(status).decode()
+        raise AttnError(status, msg)
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return ATTN_F32
+    if t.dtype == torch.bfloat16:
+        return ATTN_BF16
+    if t.dtype == torch.int8:
+        return ATTN_INT8
+    raise TypeError(f"unsupported q/k dtype {t.dtype}")
+
+
+def _contig(*ts):
+    for t in ts:
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("tensors must be contiguous CUDA tensors")
+
+
+def make_problem(q, *, causal: bool, p_bf16: bool = True, softmax_scale: float = 0.0,
+                 dtype: Optional[int] = None) -> AttnProblem:
+    b, h, n, d = q.shape
+    return AttnProblem(b, h, n, d, int(bool(causal)),
+                       _dtype_code(q) if dtype is None else dtype, int(bool(p_bf16)),
+                       float(softmax_scale), 0, 0.0)
+
+
+def _out_like(q, v):
+    import torch
+    if q.dtype == torch.int8:
+        return torch.empty(q.shape[:-1] + (v.shape[-1],), dtype=v.dtype, device=v.device)
+    return torch.empty_like(v)
+
+
+def attn_fwd_flash(q, k, v, *, causal: bool, p_bf16: bool = True, softmax_scale: float = 0.0,
+                   q_scale=None, k_scale=None, out=None, lse=None, stream=None):
+    """FlashAttention forward; returns ``out`` ([B,H,N,d], dtype of v)."""
+    _contig(q, k, v, q_scale, k_scale, out, lse)
+    out = _out_like(q, v) if out is None else out
+    prob = make_problem(q, causal=causal, p_bf16=p_bf16, softmax_scale=softmax_scale)
+    _check(load().attn_fwd_flash(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(q_scale),
+                                 _ptr(k_scale), _ptr(out), _ptr(lse), _stream(stream)))
+    return out
+
+
+def attn_fwd_flash_debug_s(q, k, v, *, causal: bool, p_bf16: bool = True,
+                           softmax_scale: float = 0.0, q_scale=None, k_scale=None, out=None,
+                           s_out=None, stream=None):
+    """Int8 flash forward that also writes its int32 score tiles to s_out."""
+    _contig(q, k, v, q_scale, k_scale, out, s_out)
+    out = _out_like(q, v) if out is None else out
+    prob = make_problem(q, causal=causal, p_bf16=p_bf16, softmax_scale=softmax_scale)
+    _check(load().attn_fwd_flash_debug_s(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v),
+                                         _ptr(q_scale), _ptr(k_scale), _ptr(out), _ptr(s_out),
+                                         _stream(stream)))
+    return out, s_out
+
+
+def attn_baseline_workspace_size(prob: AttnProblem) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load().attn_baseline_workspace_size(ctypes.byref(prob), ctypes.byref(n)))
+    return n.value
+
+
+def attn_fwd_baseline(q, k, v, *, causal: bool, p_bf16: bool = True, softmax_scale: float = 0.0,
+                      q_scale=None, k_scale=None, workspace=None, out=None, stream=None):
+    """Baseline attention (S and P in the workspace); returns (out, workspace)."""
+    import torch
+    _contig(q, k, v, q_scale, k_scale, out, workspace)
+    out = _out_like(q, v) if out is None else out
+    prob = make_problem(q, causal=causal, p_bf16=p_bf16, softmax_scale=softmax_scale)
+    need = attn_baseline_workspace_size(prob)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(load().attn_fwd_baseline(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(q_scale),
+                                    _ptr(k_scale), _ptr(workspace), nbytes, _ptr(out),
+                                    _stream(stream)))
+    return out, workspace
+
+
+def attn_deviation_scratch_size(n: int) -> int:
+    b = ctypes.c_size_t(0)
+    _check(load().attn_deviation_scratch_size(int(n), ctypes.byref(b)))
+    return b.value
+
+
+def attn_deviation(o_test, o_ref, *, scratch=None, stream=None) -> dict:
+    """Deviation summary of o_test (fp32/bf16) against o_ref (fp64), on the GPU."""
+    import torch
+    _contig(o_test, o_ref, scratch)
+    if o_ref.dtype != torch.float64:
+        raise TypeError("o_ref must be float64")
+    n = o_test.numel()
+    if o_ref.numel() != n:
+        raise ValueError("o_test and o_ref differ in size")
+    need = attn_deviation_scratch_size(n)
+    if scratch is None:
+        scratch = torch.empty(max(need, 1), dtype=torch.uint8, device=o_test.device)
+    res = AttnDeviation()
+    _check(load().attn_deviation(_ptr(o_test), _dtype_code(o_test), _ptr(o_ref), n, _ptr(scratch),
+                                 scratch.numel() * scratch.element_size(), ctypes.byref(res),
+                                 _stream(stream)))
+    return res.as_dict()
+
+
+def attn_quantize_int8(x, *, codes=None, scales=None, stream=None):
+    """Per-row int8 quantisation of fp32 x[..., d]; returns (codes, scales)."""
+    import torch
+    _contig(x, codes, scales)
+    if x.dtype != torch.float32:
+        raise TypeError("x must be float32")
+    d = x.shape[-1]
+    rows = x.numel() // d if d else 0
+    codes = torch.empty(x.shape, dtype=torch.int8, device=x.device) if codes is None else codes
+    scales = (torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
+              if scales is None else scales)
+    _check(load().attn_quantize_int8(_ptr(x), rows, d, _ptr(codes), _ptr(scales),
+                                     _stream(stream)))
+    return codes, scales
+
+
+def attn_version() -> str:
+    return load().attn_version().decode()
+
+
+def flops(batch: int, heads: int, seq_len: int, head_dim: int, causal: bool) -> float:
+    """MFMA contraction flops over visible (query, key) pairs (QK^T and PV)."""
+    if causal:
+        return 2.0 * batch * heads * head_dim * seq_len * (seq_len + 1)
+    return 4.0 * batch * heads * seq_len * seq_len * head_dim
+
+
+def default_scale(head_dim: int) -> float:
+    return 1.0 / math.sqrt(head_dim)

@@ -1,0 +1,324 @@
+// Baseline attention for gfx950: the score matrix is materialised in HBM.
+//
+// "Is Flash Attention Stable?" (abstract) compares FlashAttention with the
+// plain, non-fused attention ("Baseline Attention") in an isolated forward
+// pass.  Three kernels on one stream, each a separate pass over HBM:
+//   K1 scores : S = scale * Q K^T for all N x N (query, key) pairs, fp32
+//               (int8 Q/K: the exact int32 products Qc Kc^T, unscaled)
+//   K2 softmax: per row, the causal mask, the row max, exp, the row sum and
+//               the normalised P = e / sum in fp32, stored as bf16 (RNE) or
+//               fp32
+//   K3 pv     : O = P V with fp32 accumulation (bf16 MFMA when P and V are
+//               both bf16, fp32 MFMA otherwise)
+// The kernels are HBM-bound by design (about 12 bytes of traffic per score
+// element with bf16 P); the naive path computes and stores every one of the
+// N^2 entries, masked or not.
+#include <type_traits>
+
+#include "device.hpp"
+#include "launch.hpp"
+
+namespace pn {
+namespace {
+
+constexpr int kThreads = 256;
+
+// ---------------------------------------------------------------------------
+// K1: S tile of 128 queries x 128 keys per workgroup; wave w owns 32 query
+// rows and all 128 keys (4 MFMA tiles).  Operands come straight from global
+// memory (16-byte loads along d), the output leaves in 128-byte row segments.
+// ---------------------------------------------------------------------------
+template <int D, int QK>  // QK: 0 bf16, 1 int8, 2 fp32
+__global__ __launch_bounds__(kThreads) void scores_kernel(const void* qp, const void* kp,
+                                                         void* sp, int N, float scale) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 5, n = lane & 31;
+  const int64_t bh = blockIdx.z;
+  const int i0 = blockIdx.y * 128 + wave * 32;
+  const int j0 = blockIdx.x * 128;
+  const int64_t hoff = bh * (int64_t)N * D;
+  const int qi = i0 + n;  // A-operand row of this lane
+  if constexpr (QK == 0 || QK == 1) {
+    using T = typename std::conditional<QK == 0, uint16_t, int8_t>::type;
+    constexpr int EPC = 16 / (int)sizeof(T);
+    constexpr int ST = D / (2 * EPC);
+    const T* Q = (const T*)qp + hoff;
+    const T* K = (const T*)kp + hoff;
+    i32x4 a[ST];
+#pragma unroll
+    for (int t = 0; t < ST; ++t)
+      a[t] = qi < N ? *(const i32x4*)(Q + (int64_t)qi * D + 2 * EPC * t + EPC * g)
+                    : i32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt) {
+      const int kj = j0 + 32 * jt + n;  // B-operand column of this lane
+      using Acc = typename std::conditional<QK == 0, f32x16, i32x16>::type;
+      Acc acc = {};
+#pragma unroll
+      for (int t = 0; t < ST; ++t) {
+        const i32x4 b = kj < N ? *(const i32x4*)(K + (int64_t)kj * D + 2 * EPC * t + EPC * g)
+                               : i32x4{0, 0, 0, 0};
+        if constexpr (QK == 0)
+          acc = mfma_bf16(__builtin_bit_cast(bf16x8, a[t]), __builtin_bit_cast(bf16x8, b), acc);
+        else
+          acc = mfma_i8(a[t], b, acc);
+      }
+      if (kj < N) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int i = i0 + 8 * (r >> 2) + 4 * g + (r & 3);
+          if (i < N) {
+            const int64_t off = (bh * N + i) * (int64_t)N + kj;
+            if constexpr (QK == 0)
+              ((float*)sp)[off] = acc[r] * scale;
+            else
+              ((int32_t*)sp)[off] = acc[r];
+          }
+        }
+      }
+    }
+  } else {
+    const float* Q = (const float*)qp + hoff;
+    const float* K = (const float*)kp + hoff;
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt) {
+      const int kj = j0 + 32 * jt + n;
+      f32x16 acc = {};
+      for (int t = 0; t < D / 2; ++t) {
+        const float a = qi < N ? Q[(int64_t)qi * D + 2 * t + g] : 0.f;
+        const float b = kj < N ? K[(int64_t)kj * D + 2 * t + g] : 0.f;
+        acc = mfma_f32(a, b, acc);
+      }
+      if (kj < N) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int i = i0 + 8 * (r >> 2) + 4 * g + (r & 3);
+          if (i < N) ((float*)sp)[(bh * N + i) * (int64_t)N + kj] = acc[r] * scale;
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// K2: one workgroup per score row: mask, max, exp, sum, normalise, store P.
+// Fixed thread-to-element map and reduction tree: deterministic.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float block_reduce(float x, bool is_max, float* red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float y = __shfl_xor(x, off);
+    x = is_max ? fmaxf(x, y) : x + y;
+  }
+  __syncthreads();
+  if (lane == 0) red[wave] = x;
+  __syncthreads();
+  float r = red[0];
+#pragma unroll
+  for (int w = 1; w < kThreads / 64; ++w) r = is_max ? fmaxf(r, red[w]) : r + red[w];
+  return r;
+}
+
+template <bool INT8S, bool PBF16>
+__global__ __launch_bounds__(kThreads) void softmax_kernel(const void* sp, void* pp,
+                                                          const float* q_scale,
+                                                          const float* k_scale, int N,
+                                                          int causal, float scale) {
+  __shared__ float red[kThreads / 64];
+  const int i = blockIdx.x;
+  const int64_t bh = blockIdx.y;
+  const int64_t row = (bh * N + i) * (int64_t)N;
+  const int jend = causal ? i + 1 : N;  // visible keys: j < jend
+  const float sqc = INT8S ? q_scale[bh * N + i] * scale : 0.f;
+  auto score = [&](int j) -> float {
+    if constexpr (INT8S)
+      return (float)((const int32_t*)sp)[row + j] * (k_scale[bh * N + j] * sqc);
+    else
+      return ((const float*)sp)[row + j];
+  };
+  float m = -INFINITY;
+  for (int j = threadIdx.x; j < jend; j += kThreads) m = fmaxf(m, score(j));
+  m = block_reduce(m, true, red);
+  float sum = 0.f;
+  for (int j = threadIdx.x; j < jend; j += kThreads)
+    sum += exp2_approx((score(j) - m) * kLog2e);
+  sum = block_reduce(sum, false, red);
+  const float inv = 1.f / sum;
+  for (int j = threadIdx.x; j < N; j += kThreads) {
+    const float pv = j < jend ? exp2_approx((score(j) - m) * kLog2e) * inv : 0.f;
+    if constexpr (PBF16)
+      ((uint16_t*)pp)[row + j] = f32_to_bf16(pv);
+    else
+      ((float*)pp)[row + j] = pv;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// K3: O = P V.  Workgroup = 128 query rows (4 waves x 32); keys in blocks of
+// 64 staged in LDS (P tile and V tile, both row-major).  Each wave forms
+// O^T = V^T P^T: V^T through the transposing LDS read, P^T straight from its
+// row-major tile.
+// ---------------------------------------------------------------------------
+template <int D, typename PT, typename VT>
+__global__ __launch_bounds__(kThreads) void pv_kernel(const void* pp, const void* vp, void* op,
+                                                     int N) {
+  constexpr bool BF16MMA = sizeof(PT) == 2 && sizeof(VT) == 2;
+  constexpr int PS = 64 + 16 / (int)sizeof(PT);                 // P tile row stride
+  constexpr int VS = D + (sizeof(VT) == 2 ? 32 : 4);            // V tile row stride
+  constexpr int PCPR = 64 * (int)sizeof(PT) / 16, PCH = 128 * PCPR / kThreads;
+  constexpr int VCPR = D * (int)sizeof(VT) / 16, VCH = 64 * VCPR / kThreads;
+  constexpr int DT = D / 32;
+  __shared__ __attribute__((aligned(16))) PT p_lds[128 * PS];
+  __shared__ __attribute__((aligned(16))) VT v_lds[64 * VS];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 5, n = lane & 31;
+  const int64_t bh = blockIdx.y;
+  const int q0 = blockIdx.x * 128;
+  const PT* P = (const PT*)pp + bh * (int64_t)N * N;
+  const VT* V = (const VT*)vp + bh * (int64_t)N * D;
+  f32x16 oacc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x16{};
+  constexpr int EPC_P = 16 / (int)sizeof(PT);
+  for (int kb = 0; kb < N; kb += 64) {
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < PCH; ++i) {
+      const int c = tid + i * kThreads, row = c / PCPR, col = c % PCPR;
+      const int q = q0 + row, key = kb + EPC_P * col;
+      i32x4 val = {0, 0, 0, 0};
+      if (q < N) {
+        const PT* src = P + (int64_t)q * N + key;
+        if (key + EPC_P <= N && (((uintptr_t)src) & 15) == 0) {
+          val = *(const i32x4*)src;
+        } else {
+          PT tmp[EPC_P];
+#pragma unroll
+          for (int e = 0; e < EPC_P; ++e) tmp[e] = key + e < N ? src[e] : PT(0);
+          __builtin_memcpy(&val, tmp, 16);
+        }
+      }
+      *(i32x4*)((char*)(p_lds + row * PS) + 16 * col) = val;
+    }
+#pragma unroll
+    for (int i = 0; i < VCH; ++i) {
+      const int c = tid + i * kThreads, row = c / VCPR, col = c % VCPR;
+      const int key = kb + row;
+      *(i32x4*)((char*)(v_lds + row * VS) + 16 * col) =
+          key < N ? *(const i32x4*)((const char*)(V + (int64_t)key * D) + 16 * col)
+                  : i32x4{0, 0, 0, 0};
+    }
+    __syncthreads();
+    const PT* prow = p_lds + (32 * wave + n) * PS;
+    if constexpr (BF16MMA) {
+      const int vrow = 8 * g + ((lane & 15) >> 2);
+      const int vcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const bf16x8 pb = __builtin_bit_cast(bf16x8, *(const i32x4*)(prow + 16 * u + 8 * g));
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const VT* src = v_lds + (16 * u + vrow) * VS + 32 * dt + vcol;
+          oacc[dt] = mfma_bf16(join_bf16x8(lds_read_tr16(src), lds_read_tr16(src + 4 * VS)), pb,
+                               oacc[dt]);
+        }
+      }
+    } else {
+      for (int t = 0; t < 32; ++t) {
+        const int key = 2 * t + g;
+        float pv;
+        if constexpr (sizeof(PT) == 2) pv = bf16_to_f32(prow[key]);
+        else pv = prow[key];
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          float vv;
+          if constexpr (sizeof(VT) == 2) vv = bf16_to_f32(v_lds[key * VS + 32 * dt + n]);
+          else vv = v_lds[key * VS + 32 * dt + n];
+          oacc[dt] = mfma_f32(vv, pv, oacc[dt]);
+        }
+      }
+    }
+  }
+  const int q = q0 + 32 * wave + n;
+  if (q < N) {
+    VT* dst = (VT*)op + (bh * N + q) * (int64_t)D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int b4 = 0; b4 < 4; ++b4) {
+        const int d0 = 32 * dt + 8 * b4 + 4 * g;
+        const float x0 = oacc[dt][4 * b4], x1 = oacc[dt][4 * b4 + 1];
+        const float x2 = oacc[dt][4 * b4 + 2], x3 = oacc[dt][4 * b4 + 3];
+        if constexpr (sizeof(VT) == 2) {
+          uint2 w;
+          w.x = (uint32_t)f32_to_bf16(x0) | ((uint32_t)f32_to_bf16(x1) << 16);
+          w.y = (uint32_t)f32_to_bf16(x2) | ((uint32_t)f32_to_bf16(x3) << 16);
+          *(uint2*)(dst + d0) = w;
+        } else {
+          *(float4*)(dst + d0) = make_float4(x0, x1, x2, x3);
+        }
+      }
+  }
+}
+
+template <int D>
+hipError_t launch_scores(const AttnArgs& a, void* s, hipStream_t st) {
+  const int N = (int)a.seq_len;
+  const int t = (N + 127) / 128;
+  dim3 grid(t, t, (unsigned)(a.batch * a.heads));
+  if (a.dtype == kBF16)
+    hipLaunchKernelGGL((scores_kernel<D, 0>), grid, dim3(kThreads), 0, st, a.q, a.k, s, N, a.scale);
+  else if (a.dtype == kINT8)
+    hipLaunchKernelGGL((scores_kernel<D, 1>), grid, dim3(kThreads), 0, st, a.q, a.k, s, N, a.scale);
+  else
+    hipLaunchKernelGGL((scores_kernel<D, 2>), grid, dim3(kThreads), 0, st, a.q, a.k, s, N, a.scale);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_pv(const AttnArgs& a, const void* p, hipStream_t st) {
+  const int N = (int)a.seq_len;
+  dim3 grid((N + 127) / 128, (unsigned)(a.batch * a.heads));
+  const bool vf32 = a.dtype == kF32;
+  if (a.p_bf16 && !vf32)
+    hipLaunchKernelGGL((pv_kernel<D, uint16_t, uint16_t>), grid, dim3(kThreads), 0, st, p, a.v, a.o, N);
+  else if (a.p_bf16 && vf32)
+    hipLaunchKernelGGL((pv_kernel<D, uint16_t, float>), grid, dim3(kThreads), 0, st, p, a.v, a.o, N);
+  else if (!vf32)
+    hipLaunchKernelGGL((pv_kernel<D, float, uint16_t>), grid, dim3(kThreads), 0, st, p, a.v, a.o, N);
+  else
+    hipLaunchKernelGGL((pv_kernel<D, float, float>), grid, dim3(kThreads), 0, st, p, a.v, a.o, N);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t baseline_workspace_bytes(int64_t bh, int64_t n, int p_bf16) {
+  const size_t elems = (size_t)bh * (size_t)n * (size_t)n;
+  return elems * 4 + elems * (p_bf16 ? 2 : 4);
+}
+
+hipError_t launch_baseline(const AttnArgs& a, void* workspace, hipStream_t st) {
+  const int64_t bh = a.batch * a.heads;
+  const int N = (int)a.seq_len;
+  void* s = workspace;
+  void* p = (char*)workspace + (size_t)bh * N * (size_t)N * 4;
+  hipError_t e = a.head_dim == 64 ? launch_scores<64>(a, s, st) : launch_scores<128>(a, s, st);
+  if (e != hipSuccess) return e;
+  dim3 grid2((unsigned)N, (unsigned)bh);
+  const bool i8 = a.dtype == kINT8;
+  if (i8 && a.p_bf16)
+    hipLaunchKernelGGL((softmax_kernel<true, true>), grid2, dim3(kThreads), 0, st, s, p, a.q_scale, a.k_scale, N, a.causal, a.scale);
+  else if (i8)
+    hipLaunchKernelGGL((softmax_kernel<true, false>), grid2, dim3(kThreads), 0, st, s, p, a.q_scale, a.k_scale, N, a.causal, a.scale);
+  else if (a.p_bf16)
+    hipLaunchKernelGGL((softmax_kernel<false, true>), grid2, dim3(kThreads), 0, st, s, p, a.q_scale, a.k_scale, N, a.causal, a.scale);
+  else
+    hipLaunchKernelGGL((softmax_kernel<false, false>), grid2, dim3(kThreads), 0, st, s, p, a.q_scale, a.k_scale, N, a.causal, a.scale);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return a.head_dim == 64 ? launch_pv<64>(a, p, st) : launch_pv<128>(a, p, st);
+}
+
+}  // namespace pn

@@ -1,0 +1,143 @@
+// Deviation summary of a low-precision attention output against a
+// high-precision reference ("Is Flash Attention Stable?", abstract: numeric
+// deviation of an isolated forward pass; O_lp and O_hp in "Why Low-Precision
+// Transformer Training Fails", Figure 5).
+//
+// Two passes with a fixed element-to-thread map and fixed reduction trees, so
+// the fp64 sums are bitwise reproducible run to run:
+//   pass 1: G workgroups, each over one contiguous chunk, write a partial
+//   pass 2: one workgroup folds the G partials in index order
+// HBM-bound: reads n * (2 or 4) bytes of o_test and 8n bytes of o_ref once.
+#include "device.hpp"
+#include "launch.hpp"
+
+namespace pn {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kMaxBlocks = 1024;
+
+struct Partial {
+  double max_abs;  // -1 when no finite element was seen
+  double sum_abs, sum_signed, sum_sq, max_ref;
+  int64_t argmax, nonfinite;
+};
+
+__device__ __forceinline__ void fold(Partial& a, const Partial& b) {
+  if (b.max_abs > a.max_abs || (b.max_abs == a.max_abs && b.argmax < a.argmax)) {
+    a.max_abs = b.max_abs;
+    a.argmax = b.argmax;
+  }
+  a.sum_abs += b.sum_abs;
+  a.sum_signed += b.sum_signed;
+  a.sum_sq += b.sum_sq;
+  a.max_ref = fmax(a.max_ref, b.max_ref);
+  a.nonfinite += b.nonfinite;
+}
+
+__device__ __forceinline__ Partial empty_partial() {
+  Partial p;
+  p.max_abs = -1.0;
+  p.sum_abs = p.sum_signed = p.sum_sq = 0.0;
+  p.max_ref = 0.0;
+  p.argmax = INT64_MAX;
+  p.nonfinite = 0;
+  return p;
+}
+
+// Fixed-shape tree over the workgroup; result in lds[0].
+__device__ void tree(Partial& mine, Partial* lds) {
+  lds[threadIdx.x] = mine;
+  __syncthreads();
+  for (int s = kThreads / 2; s >= 1; s >>= 1) {
+    if ((int)threadIdx.x < s) fold(lds[threadIdx.x], lds[threadIdx.x + s]);
+    __syncthreads();
+  }
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void deviation_pass1(const void* t, const double* ref,
+                                                           int64_t n, int64_t chunk,
+                                                           Partial* parts) {
+  __shared__ Partial lds[kThreads];
+  const int64_t lo = (int64_t)blockIdx.x * chunk;
+  const int64_t hi = lo + chunk < n ? lo + chunk : n;
+  Partial mine = empty_partial();
+  for (int64_t i = lo + threadIdx.x; i < hi; i += kThreads) {
+    const double x = BF16 ? (double)bf16_to_f32(((const uint16_t*)t)[i]) : (double)((const float*)t)[i];
+    const double r = ref[i];
+    const double e = x - r;
+    if (isfinite(r)) mine.max_ref = fmax(mine.max_ref, fabs(r));
+    if (!isfinite(e)) {
+      mine.nonfinite += 1;
+      continue;
+    }
+    const double ae = fabs(e);
+    if (ae > mine.max_abs) {  // ascending i per thread: the first maximum wins
+      mine.max_abs = ae;
+      mine.argmax = i;
+    }
+    mine.sum_abs += ae;
+    mine.sum_signed += e;
+    mine.sum_sq += e * e;
+  }
+  tree(mine, lds);
+  if (threadIdx.x == 0) parts[blockIdx.x] = lds[0];
+}
+
+__global__ __launch_bounds__(kThreads) void deviation_pass2(const Partial* parts, int nparts,
+                                                           DeviationRecord* out, int64_t n) {
+  __shared__ Partial lds[kThreads];
+  Partial mine = empty_partial();
+  for (int i = threadIdx.x; i < nparts; i += kThreads) fold(mine, parts[i]);
+  tree(mine, lds);
+  if (threadIdx.x == 0) {
+    const Partial& p = lds[0];
+    DeviationRecord r;
+    r.max_abs = p.max_abs;
+    r.sum_abs = p.sum_abs;
+    r.sum_signed = p.sum_signed;
+    r.sum_sq = p.sum_sq;
+    r.max_ref_abs = p.max_ref;
+    r.n_nonfinite = p.nonfinite;
+    r.argmax = p.max_abs < 0 ? -1 : p.argmax;
+    r.n = n;
+    *out = r;
+  }
+}
+
+int blocks_for(int64_t n) {
+  int64_t b = (n + (int64_t)kThreads * 64 - 1) / ((int64_t)kThreads * 64);
+  if (b < 1) b = 1;
+  if (b > kMaxBlocks) b = kMaxBlocks;
+  return (int)b;
+}
+
+}  // namespace
+
+size_t deviation_scratch_bytes(int64_t n) {
+  return (size_t)blocks_for(n) * sizeof(Partial) + sizeof(DeviationRecord) + 256;
+}
+
+hipError_t launch_deviation(const void* o_test, int o_dtype, const double* o_ref, int64_t n,
+                            void* scratch, DeviationRecord* out_host, hipStream_t st) {
+  const int nb = blocks_for(n);
+  const int64_t chunk = (n + nb - 1) / nb;
+  Partial* parts = (Partial*)scratch;
+  DeviationRecord* rec =
+      (DeviationRecord*)(((uintptr_t)(parts + nb) + 255) & ~(uintptr_t)255);
+  if (o_dtype == kBF16)
+    hipLaunchKernelGGL((deviation_pass1<true>), dim3(nb), dim3(kThreads), 0, st, o_test, o_ref, n, chunk, parts);
+  else
+    hipLaunchKernelGGL((deviation_pass1<false>), dim3(nb), dim3(kThreads), 0, st, o_test, o_ref, n, chunk, parts);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(deviation_pass2, dim3(1), dim3(kThreads), 0, st, parts, nb, rec, n);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e = hipMemcpyAsync(out_host, rec, sizeof(DeviationRecord), hipMemcpyDeviceToHost, st);
+  if (e != hipSuccess) return e;
+  return hipStreamSynchronize(st);
+}
+
+}  // namespace pn

@@ -1,0 +1,82 @@
+// Device-side helpers shared by the pnattn kernels (gfx950 / CDNA4 only).
+//
+// Register layouts used throughout (measured on gfx950 with an in-bounds
+// lane-layout check of each builtin):
+//  * 32x32 MFMA accumulator (bf16, i8 and f32 inputs alike): lane l, register
+//    r holds C[8*(r/4) + 4*(l/32) + r%4][l%32].
+//  * v_mfma_f32_32x32x16_bf16: A lane l holds A[l%32][8*(l/32) + e], e=0..7;
+//    B lane l holds B[8*(l/32) + e][l%32].
+//  * v_mfma_i32_32x32x32_i8: the same with 16 int8 per lane, k = 16*(l/32)+e.
+//  * v_mfma_f32_32x32x2f32: one float per lane, k = l/32.
+//  * ds_read_b64_tr_b16: inside each group of 16 lanes, lane i receives
+//    element i%4 of the 4-element rows addressed by lanes 4e + i/4, e=0..3.
+//  * permlane32_swap(x, x) returns {x[l%32], x[32 + l%32]} in every lane.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ float exp2_approx(float x) {
+  return __builtin_amdgcn_exp2f(x);  // v_exp_f32; exp2(0) == 1 exactly
+}
+
+// max / sum of a value over the lane pair (l, l ^ 32); both lanes get the
+// bitwise-same result (low-half operand first).
+__device__ __forceinline__ float pair32_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x),
+                                            __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair32_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x),
+                                            __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// bf16 bit pattern <-> float (exact widening; RNE narrowing)
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+__device__ __forceinline__ uint16_t f32_to_bf16(float x) {
+  return __builtin_bit_cast(uint16_t, (__bf16)x);
+}
+__device__ __forceinline__ float round_to_bf16(float x) {
+  return bf16_to_f32(f32_to_bf16(x));
+}
+
+// Transposed 64-bit LDS read (ds_read_b64_tr_b16) from a generic pointer
+// into LDS.
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+__device__ __forceinline__ i16x4 lds_read_tr16(const void* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_i16x4*)((__attribute__((address_space(3))) char*)(p)));
+}
+__device__ __forceinline__ bf16x8 join_bf16x8(i16x4 lo, i16x4 hi) {
+  i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+__device__ __forceinline__ f32x16 mfma_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ i32x16 mfma_i8(i32x4 a, i32x4 b, i32x16 c) {
+  return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma_f32(float a, float b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+}  // namespace pn

@@ -1,0 +1,50 @@
+// Host-side launchers behind the C ABI (internal; not installed).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pn {
+
+enum DType : int { kF32 = 0, kBF16 = 1, kINT8 = 2 };
+
+struct AttnArgs {
+  const void* q = nullptr;
+  const void* k = nullptr;
+  const void* v = nullptr;
+  const float* q_scale = nullptr;
+  const float* k_scale = nullptr;
+  void* o = nullptr;
+  float* lse = nullptr;
+  int32_t* s_dbg = nullptr;
+  int64_t batch = 0, heads = 0, seq_len = 0;
+  int head_dim = 0;
+  int causal = 0;
+  int dtype = kBF16;
+  int p_bf16 = 1;
+  float scale = 0.f;  // resolved softmax scale (> 0)
+};
+
+// Flash forward; returns the launch status.
+hipError_t launch_flash(const AttnArgs& a, hipStream_t stream);
+
+// Baseline: workspace holds S [B,H,N,N] (4 B/elem) then P (2 or 4 B/elem).
+size_t baseline_workspace_bytes(int64_t bh, int64_t n, int p_bf16);
+hipError_t launch_baseline(const AttnArgs& a, void* workspace,
+                           hipStream_t stream);
+
+// Deviation summary; partials and the final record live in scratch.
+size_t deviation_scratch_bytes(int64_t n);
+struct DeviationRecord {
+  double max_abs, sum_abs, sum_signed, sum_sq, max_ref_abs;
+  int64_t n_nonfinite, argmax, n;
+};
+hipError_t launch_deviation(const void* o_test, int o_dtype,
+                            const double* o_ref, int64_t n, void* scratch,
+                            DeviationRecord* out_host, hipStream_t stream);
+
+hipError_t launch_quantize(const float* x, int64_t rows, int64_t d,
+                           int8_t* codes, float* scales, hipStream_t stream);
+
+}  // namespace pn
