@@ -41,17 +41,41 @@ enum QKKind { QK_BF16 = 0, QK_I8 = 1, QK_F32 = 2 };
 // widened exactly (V stored as bf16 or as fp32).
 enum PVKind { PV_BF16 = 0, PV_F32_VBF16 = 1, PV_F32_VF32 = 2 };
 
-constexpr int kBR = 128;  // query rows per workgroup
-constexpr int kBC = 64;   // keys per step
-constexpr int kThreads = 256;
+constexpr int kWaves = 4;            // waves per workgroup (one per SIMD)
+constexpr int kThreads = 64 * kWaves;
+constexpr int kBR = 32 * kWaves;     // query rows per workgroup
+constexpr int kBC = 64;              // keys per step
 
 template <int QK> struct QKTraits;
-template <> struct QKTraits<QK_BF16> { using T = uint16_t; static constexpr int kPad = 8; };
-template <> struct QKTraits<QK_I8> { using T = int8_t; static constexpr int kPad = 16; };
-template <> struct QKTraits<QK_F32> { using T = float; static constexpr int kPad = 4; };
+template <> struct QKTraits<QK_BF16> { using T = uint16_t; };
+template <> struct QKTraits<QK_I8> { using T = int8_t; };
+template <> struct QKTraits<QK_F32> { using T = float; };
+template <int PV> struct VTraits { using T = uint16_t; };
+template <> struct VTraits<PV_F32_VF32> { using T = float; };
 
-template <int PV> struct VTraits { using T = uint16_t; static constexpr int kPad = 32; };
-template <> struct VTraits<PV_F32_VF32> { using T = float; static constexpr int kPad = 4; };
+// LDS tile geometry.  Rows are padded so that the two read patterns of the
+// kernel are free of bank conflicts: +16 bytes per K row (16 consecutive K
+// rows read the same 16-byte column), +64 bytes per V row (the transposing
+// reads touch 4 rows x 64 bytes at a time).  Tiles are whole multiples of
+// 1 KiB, the footprint of one wave-wide 16-byte buffer load into LDS.
+template <int D, int QK, int PV> struct Tile {
+  static constexpr int kRowK = D * (int)sizeof(typename QKTraits<QK>::T);
+  static constexpr int kRowV = D * (int)sizeof(typename VTraits<PV>::T);
+  static constexpr int kStrK = kRowK + 16;
+  static constexpr int kStrV = kRowV + 64;
+  static constexpr int kBytesK = kBC * kStrK;
+  static constexpr int kBytesV = kBC * kStrV;
+  static constexpr int kSegK = kBytesK / 1024;
+  static constexpr int kSegV = kBytesV / 1024;
+  static constexpr int kSegKPerWave = (kSegK + kWaves - 1) / kWaves;
+  static constexpr int kSegVPerWave = (kSegV + kWaves - 1) / kWaves;
+  static constexpr int kBytesSk = (QK == QK_I8) ? kBC * 4 : 0;
+  // [K buf0][K buf1][V buf0][V buf1][sk buf0][sk buf1]
+  static constexpr int kOffV = 2 * kBytesK;
+  static constexpr int kOffSk = kOffV + 2 * kBytesV;
+  static constexpr int kLds = kOffSk + 2 * kBytesSk;
+  static_assert(kBytesK % 1024 == 0 && kBytesV % 1024 == 0, "tiles must be whole segments");
+};
 
 struct FlashParams {
   const void* q;
@@ -80,27 +104,80 @@ template <typename T> __device__ __forceinline__ float to_f32(T x);
 template <> __device__ __forceinline__ float to_f32<uint16_t>(uint16_t x) { return bf16_to_f32(x); }
 template <> __device__ __forceinline__ float to_f32<float>(float x) { return x; }
 
+typedef __attribute__((address_space(3))) char lds_char;
+
+// Byte offset, inside one tile, that lane `lane` of segment `seg` fills, as
+// a source offset relative to the tile's first key row (or ~0 for padding
+// slots, which the bounds-checked load turns into a harmless zero fill).
+__device__ __forceinline__ uint32_t seg_src_offset(int seg, int lane, int row_bytes, int stride) {
+  const int pos = (seg * 64 + lane) * 16;
+  const int row = pos / stride, col = pos % stride;
+  return col < row_bytes ? (uint32_t)(row * row_bytes + col) : 0x7ffffff0u;
+}
+
+// Issue this wave's share of the bounds-checked 16-byte buffer loads that
+// fill K/V tile buffer `buf` with key rows kb..kb+63 (and, for int8, the 64
+// key scales).  Asynchronous: completion is awaited with vmcnt before the
+// workgroup barrier that publishes the tile.
+template <int D, int QK, int PV>
+__device__ __forceinline__ void issue_block(char* smem, int wave, int lane, int kb, int buf,
+                                            const void* kbase, const void* vbase,
+                                            const void* sbase, int n, const uint32_t* voffK,
+                                            const uint32_t* voffV) {
+  using TL = Tile<D, QK, PV>;
+  // buffer resources spanning exactly this head: key rows >= n read as zeros
+  const int nbK = n * TL::kRowK, nbV = n * TL::kRowV;
+  const __amdgpu_buffer_rsrc_t rsK =
+      __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, nbK, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rsV =
+      __builtin_amdgcn_make_buffer_rsrc((void*)vbase, (short)0, nbV, 0x00020000);
+  lds_char* lds = (lds_char*)smem;
+#pragma unroll
+  for (int i = 0; i < TL::kSegKPerWave; ++i) {
+    const int seg = wave + i * kWaves;
+    // (arguments go through locals: a template-dependent expression written
+    // straight into this builtin makes clang's host pass drop the kernel)
+    const int soff = kb * TL::kRowK;
+    lds_char* dst = lds + (buf * TL::kBytesK + seg * 1024);
+    if (TL::kSegK % kWaves == 0 || seg < TL::kSegK)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsK, dst, 16, voffK[i], soff, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < TL::kSegVPerWave; ++i) {
+    const int seg = wave + i * kWaves;
+    const int soff = kb * TL::kRowV;
+    lds_char* dst = lds + (TL::kOffV + buf * TL::kBytesV + seg * 1024);
+    if (TL::kSegV % kWaves == 0 || seg < TL::kSegV)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsV, dst, 16, voffV[i], soff, 0, 0);
+  }
+  if constexpr (QK == QK_I8) {
+    const int nbS = n * 4;
+    const __amdgpu_buffer_rsrc_t rsS =
+        __builtin_amdgcn_make_buffer_rsrc((void*)sbase, (short)0, nbS, 0x00020000);
+    const int soff = kb * 4;
+    const uint32_t voff = lane * 4;
+    lds_char* dst = lds + (TL::kOffSk + buf * TL::kBytesSk);
+    if (wave == 0) __builtin_amdgcn_raw_ptr_buffer_load_lds(rsS, dst, 4, voff, soff, 0, 0);
+  }
+}
+
+// Two waves per SIMD (two workgroups per CU) where the LDS tiles allow it.
+template <int D, int QK, int PV>
+constexpr int min_waves_per_simd() { return Tile<D, QK, PV>::kLds * 2 <= 160 * 1024 ? 2 : 1; }
+
 template <int D, int QK, int PV, bool CAUSAL, bool DEBUG_S>
-__global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
+__global__ __launch_bounds__(kThreads, (min_waves_per_simd<D, QK, PV>()))
+void flash_fwd_kernel(FlashParams p) {
   using QT = typename QKTraits<QK>::T;
   using VT = typename VTraits<PV>::T;
-  constexpr int KS = D + QKTraits<QK>::kPad;  // K tile row stride (elements)
-  constexpr int VS = D + VTraits<PV>::kPad;   // V tile row stride (elements)
-  constexpr int KCPR = D * (int)sizeof(QT) / 16;
-  constexpr int VCPR = D * (int)sizeof(VT) / 16;
-  constexpr int KCH = kBC * KCPR / kThreads;
-  constexpr int VCH = kBC * VCPR / kThreads;
-  static_assert(KCH >= 1 && VCH >= 1, "tile too small for the staging map");
-  static_assert(kBC * KCPR % kThreads == 0 && kBC * VCPR % kThreads == 0, "");
+  using TL = Tile<D, QK, PV>;
   constexpr int DT = D / 32;  // 32-row d subtiles of O^T
 
-  __shared__ __attribute__((aligned(16))) QT k_lds[kBC * KS];
-  __shared__ __attribute__((aligned(16))) VT v_lds[kBC * VS];
-  __shared__ float sk_lds[kBC];
+  __shared__ __attribute__((aligned(1024))) char smem[TL::kLds];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5;
   const int n = lane & 31;
   const int N = p.n;
@@ -112,8 +189,6 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
   const bool qvalid = qrow < N;
   const int64_t hoff = bh * (int64_t)N * D;
   const QT* Qg = (const QT*)p.q + hoff;
-  const QT* Kg = (const QT*)p.k + hoff;
-  const VT* Vg = (const VT*)p.v + hoff;
 
   // ---- this lane's query row as the B operand of S^T = K Q^T (registers)
   constexpr int QST = (QK == QK_BF16) ? D / 16 : (QK == QK_I8 ? D / 32 : D / 2);
@@ -135,44 +210,17 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
       sq_log2 = qvalid ? p.q_scale[bh * N + qrow] * p.scale_log2 : 0.f;
   }
 
-  // ---- K/V block staging: global -> registers -> LDS (coalesced 16 B)
-  i32x4 kreg[KCH], vreg[VCH];
-  float skreg = 0.f;
-  auto load_block = [&](int kb) {
+  // ---- K/V block streaming: bounds-checked buffer loads straight into LDS
+  const void* kbase = (const char*)p.k + hoff * (int64_t)sizeof(QT);
+  const void* vbase = (const char*)p.v + hoff * (int64_t)sizeof(VT);
+  const void* sbase = (QK == QK_I8) ? (const void*)(p.k_scale + bh * N) : nullptr;
+  uint32_t voffK[TL::kSegKPerWave], voffV[TL::kSegVPerWave];
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int c = tid + i * kThreads, row = c / KCPR, col = c % KCPR;
-      const int key = kb + row;
-      kreg[i] = key < N ? *(const i32x4*)((const char*)(Kg + (int64_t)key * D) + 16 * col)
-                        : i32x4{0, 0, 0, 0};
-    }
+  for (int i = 0; i < TL::kSegKPerWave; ++i)
+    voffK[i] = seg_src_offset(wave + i * kWaves, lane, TL::kRowK, TL::kStrK);
 #pragma unroll
-    for (int i = 0; i < VCH; ++i) {
-      const int c = tid + i * kThreads, row = c / VCPR, col = c % VCPR;
-      const int key = kb + row;
-      vreg[i] = key < N ? *(const i32x4*)((const char*)(Vg + (int64_t)key * D) + 16 * col)
-                        : i32x4{0, 0, 0, 0};
-    }
-    if constexpr (QK == QK_I8) {
-      if (tid < kBC) skreg = (kb + tid < N) ? p.k_scale[bh * N + kb + tid] : 0.f;
-    }
-  };
-  auto store_block = [&]() {
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int c = tid + i * kThreads, row = c / KCPR, col = c % KCPR;
-      *(i32x4*)((char*)(k_lds + row * KS) + 16 * col) = kreg[i];
-    }
-#pragma unroll
-    for (int i = 0; i < VCH; ++i) {
-      const int c = tid + i * kThreads, row = c / VCPR, col = c % VCPR;
-      *(i32x4*)((char*)(v_lds + row * VS) + 16 * col) = vreg[i];
-    }
-    if constexpr (QK == QK_I8) {
-      if (tid < kBC) sk_lds[tid] = skreg;
-    }
-  };
-
+  for (int i = 0; i < TL::kSegVPerWave; ++i)
+    voffV[i] = seg_src_offset(wave + i * kWaves, lane, TL::kRowV, TL::kStrV);
   const int kend = CAUSAL ? min(N, q0 + kBR) : N;
   const int nblk = (kend + kBC - 1) / kBC;
   float m_run = -INFINITY;
@@ -181,25 +229,35 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x16{};
 
-  load_block(0);
+  // per-lane LDS byte offsets of the operand reads (block-independent)
+  const int k_lane = key_of_row(n) * TL::kStrK;
+  const int v_lane = (8 * g + ((lane & 15) >> 2)) * TL::kStrV +
+                     (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * (int)sizeof(VT);
+
+  issue_block<D, QK, PV>(smem, wave, lane, 0, 0, kbase, vbase, sbase, N, voffK, voffV);
   for (int j = 0; j < nblk; ++j) {
     const int kb = j * kBC;
-    __syncthreads();  // every wave is done with the previous tile
-    store_block();
-    __syncthreads();
-    if (j + 1 < nblk) load_block(kb + kBC);
+    const int buf = j & 1;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's loads of block j landed
+    __syncthreads();  // every wave's loads landed; every wave is done with block j-1
+    if (j + 1 < nblk)
+      issue_block<D, QK, PV>(smem, wave, lane, kb + kBC, buf ^ 1, kbase, vbase, sbase, N,
+                             voffK, voffV);
     if (CAUSAL && kb > q0w + 31) continue;  // block entirely above this wave's diagonal
+
+    const char* kt = (const char*)smem + buf * TL::kBytesK;
+    const char* vt = (const char*)smem + TL::kOffV + buf * TL::kBytesV;
 
     // ---- S^T = K_j Q^T for two 32-key subtiles, in log2 units
     float s[2][16];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      const int krow = 32 * ks + key_of_row(n);
+      const char* krow = kt + ks * 32 * TL::kStrK + k_lane;
       if constexpr (QK == QK_BF16) {
         f32x16 acc = {};
 #pragma unroll
         for (int t = 0; t < QST; ++t) {
-          const i32x4 a = *(const i32x4*)(k_lds + krow * KS + 16 * t + 8 * g);
+          const i32x4 a = *(const i32x4*)(krow + 32 * t + 16 * g);
           acc = mfma_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, qv[t]), acc);
         }
 #pragma unroll
@@ -208,7 +266,7 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
         i32x16 acc = {};
 #pragma unroll
         for (int t = 0; t < QST; ++t) {
-          const i32x4 a = *(const i32x4*)(k_lds + krow * KS + 32 * t + 16 * g);
+          const i32x4 a = *(const i32x4*)(krow + 32 * t + 16 * g);
           acc = mfma_i8(a, qv[t], acc);
         }
         if constexpr (DEBUG_S) {
@@ -221,14 +279,15 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
             }
           }
         }
+        const float* skt = (const float*)(smem + TL::kOffSk + buf * TL::kBytesSk);
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          s[ks][r] = (float)acc[r] * (sk_lds[32 * ks + key_of_reg(r, g)] * sq_log2);
+          s[ks][r] = (float)acc[r] * (skt[32 * ks + key_of_reg(r, g)] * sq_log2);
       } else {
         f32x16 acc = {};
 #pragma unroll
         for (int t = 0; t < QST; ++t)
-          acc = mfma_f32(k_lds[krow * KS + 2 * t + g], qf[t], acc);
+          acc = mfma_f32(*(const float*)(krow + 4 * (2 * t + g)), qf[t], acc);
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[ks][r] = acc[r] * p.scale_log2;
       }
@@ -278,15 +337,14 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
       for (int u = 0; u < 4; ++u)
 #pragma unroll
         for (int e = 0; e < 8; ++e) pb[u][e] = (__bf16)s[u >> 1][8 * (u & 1) + e];
-      const int vrow = 8 * g + ((lane & 15) >> 2);
-      const int vcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+      const char* vl = vt + v_lane;
 #pragma unroll
       for (int u = 0; u < 4; ++u)
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-          const VT* src = v_lds + (16 * u + vrow) * VS + 32 * dt + vcol;
+          const char* src = vl + 16 * u * TL::kStrV + 64 * dt;
           const i16x4 lo = lds_read_tr16(src);
-          const i16x4 hi = lds_read_tr16(src + 4 * VS);
+          const i16x4 hi = lds_read_tr16(src + 4 * TL::kStrV);
           oacc[dt] = mfma_bf16(join_bf16x8(lo, hi), pb[u], oacc[dt]);
         }
     } else {
@@ -295,7 +353,7 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float pv = p.p_round ? round_to_bf16(s[ks][r]) : s[ks][r];
-          const VT* vr = v_lds + (32 * ks + key_of_reg(r, g)) * VS + n;
+          const VT* vr = (const VT*)(vt + (32 * ks + key_of_reg(r, g)) * TL::kStrV) + n;
 #pragma unroll
           for (int dt = 0; dt < DT; ++dt)
             oacc[dt] = mfma_f32(to_f32<VT>(vr[32 * dt]), pv, oacc[dt]);
