@@ -77,9 +77,10 @@ typedef struct {
  * Algorithm 1, and the online-softmax accumulation that page's referee
  * report places at its Eq. (2)):
  * per query block, a running row max m, a running row sum l of the fp32
- * unnormalised probabilities P = exp(S - m) (P is exactly 1 at the running
- * row max, as that page's Figure 5 caption notes), and an exp-rescaled
- * fp32 output accumulator; O = acc / l at the end.  S is never stored.
+ * unnormalised probabilities P = exp(S - m) (P is 1 at the running row max,
+ * as that page's Figure 5 caption notes: to within an ulp in fp32, exactly
+ * once rounded to bf16), and an exp-rescaled fp32 output accumulator;
+ * O = acc / l at the end.  S is never stored.
  *   q, k   : [B,H,N,d] of dtype (int8 codes for ATTN_INT8)
  *   v, o   : [B,H,N,d] fp32 for ATTN_F32, bf16 otherwise
  *   q_scale, k_scale : [B,H,N] fp32, required for ATTN_INT8, else NULL

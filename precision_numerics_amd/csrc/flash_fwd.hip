@@ -6,7 +6,7 @@
 // row blocks; the online-softmax accumulation its referee report places at
 // Eq. (2)).  For each query block and each key block j in ascending order:
 //     m'  = max(m, rowmax(S_j))
-//     P_j = exp(S_j - m')              (unnormalised; exactly 1 at the max)
+//     P_j = exp(S_j - m')              (unnormalised; 1 at the running max)
 //     l'  = exp(m - m') l + rowsum(P_j)
 //     O'  = exp(m - m') O + P_j V_j
 // and finally O = O' / l'.  In exact arithmetic this is softmax(S) V for any
@@ -25,8 +25,11 @@
 //  * O^T = V_j^T P_j^T accumulates in fp32 registers (32 x d per wave).  The
 //    V^T operand comes straight from the row-major V tile through the
 //    transposing LDS read ds_read_b64_tr_b16.
-//  * Scores are kept in log2 units (scale * log2 e folded into one multiply)
-//    so every exponential is one v_exp_f32.
+//  * The row max is taken on the raw dot products (the scale is positive);
+//    each probability is then exp2(fma(s, scale*log2 e, -m)): one fma and one
+//    v_exp_f32 per score.  At the row max the fma leaves only the rounding
+//    residual of the scaled max, so P is 1 to within an ulp there and exactly
+//    1 once rounded to bf16.
 //  * Grid = (batch*heads, query tiles).  Causal launches hand out the longest
 //    query tiles first; when batch*heads is a multiple of 8 all tiles of one
 //    head land on the same XCD (round-robin dispatch), sharing its L2.
@@ -41,7 +44,7 @@ enum QKKind { QK_BF16 = 0, QK_I8 = 1, QK_F32 = 2 };
 // widened exactly (V stored as bf16 or as fp32).
 enum PVKind { PV_BF16 = 0, PV_F32_VBF16 = 1, PV_F32_VF32 = 2 };
 
-constexpr int kWaves = 4;            // waves per workgroup (one per SIMD)
+constexpr int kWaves = 8;            // two groups of four: one wave of each per SIMD
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBR = 32 * kWaves;     // query rows per workgroup
 constexpr int kBC = 64;              // keys per step
@@ -104,7 +107,6 @@ template <typename T> __device__ __forceinline__ float to_f32(T x);
 template <> __device__ __forceinline__ float to_f32<uint16_t>(uint16_t x) { return bf16_to_f32(x); }
 template <> __device__ __forceinline__ float to_f32<float>(float x) { return x; }
 
-typedef __attribute__((address_space(3))) char lds_char;
 
 // Byte offset, inside one tile, that lane `lane` of segment `seg` fills, as
 // a source offset relative to the tile's first key row (or ~0 for padding
@@ -115,59 +117,113 @@ __device__ __forceinline__ uint32_t seg_src_offset(int seg, int lane, int row_by
   return col < row_bytes ? (uint32_t)(row * row_bytes + col) : 0x7ffffff0u;
 }
 
-// Issue this wave's share of the bounds-checked 16-byte buffer loads that
-// fill K/V tile buffer `buf` with key rows kb..kb+63 (and, for int8, the 64
-// key scales).  Asynchronous: completion is awaited with vmcnt before the
-// workgroup barrier that publishes the tile.
+// Buffer resource descriptor (V#) over `bytes` bytes at `base`: loads at
+// offsets >= bytes return zeros (the hardware range check), which is how key
+// rows past the end of the sequence arrive as zeros.
+__device__ __forceinline__ i32x4 buffer_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  return i32x4{(int)(uint32_t)a, (int)(uint32_t)((a >> 32) & 0xffffu), (int)bytes, 0x00020000};
+}
+
+// One wave-wide buffer load of 16 (or 4) bytes per lane straight into LDS at
+// lds_addr + 16*lane (4*lane).  Issued through inline asm on purpose: the
+// compiler's wait-count pass cannot tell which LDS bytes such a load writes,
+// so it would make the next LDS read of ANY tile wait for it, serialising
+// the prefetch.  Every wait these loads need is explicit in the kernel
+// (s_waitcnt vmcnt(0) before the barrier that publishes a tile); compiler-
+// generated waits for other memory operations only become more conservative.
+__device__ __forceinline__ void lds_load16(i32x4 rsrc, uint32_t voff, uint32_t soff,
+                                           uint32_t lds_addr) {
+  uint32_t saved;  // M0 is reserved by the compiler: save and restore it
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %4\n\ts_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, %3 offen lds\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(rsrc), "s"(soff), "s"(lds_addr)
+      : "memory");
+}
+__device__ __forceinline__ void lds_load4(i32x4 rsrc, uint32_t voff, uint32_t soff,
+                                          uint32_t lds_addr) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %4\n\ts_nop 0\n\t"
+      "buffer_load_dword %1, %2, %3 offen lds\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(rsrc), "s"(soff), "s"(lds_addr)
+      : "memory");
+}
+
+// s_waitcnt immediate (gfx9 encoding) for vmcnt(0) with expcnt and lgkmcnt
+// left at their maxima: wait for this wave's outstanding vector-memory ops.
+constexpr int kWaitVmcnt0 = 0x0F70;
+
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+// Issue this wave's share of the loads that fill K tile buffer `buf` with
+// key rows kb..kb+63 (and, for int8, the 64 key scales).  Asynchronous.
 template <int D, int QK, int PV>
-__device__ __forceinline__ void issue_block(char* smem, int wave, int lane, int kb, int buf,
-                                            const void* kbase, const void* vbase,
-                                            const void* sbase, int n, const uint32_t* voffK,
-                                            const uint32_t* voffV) {
+__device__ __forceinline__ void issue_k(char* smem, int wave, int lane, int kb, int buf,
+                                        const void* kbase, const void* sbase, int n,
+                                        const uint32_t* voffK) {
   using TL = Tile<D, QK, PV>;
-  // buffer resources spanning exactly this head: key rows >= n read as zeros
-  const int nbK = n * TL::kRowK, nbV = n * TL::kRowV;
-  const __amdgpu_buffer_rsrc_t rsK =
-      __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, nbK, 0x00020000);
-  const __amdgpu_buffer_rsrc_t rsV =
-      __builtin_amdgcn_make_buffer_rsrc((void*)vbase, (short)0, nbV, 0x00020000);
-  lds_char* lds = (lds_char*)smem;
+  const i32x4 rsK = buffer_rsrc(kbase, (uint32_t)n * TL::kRowK);
+  const uint32_t base = lds_address(smem) + buf * TL::kBytesK;
 #pragma unroll
   for (int i = 0; i < TL::kSegKPerWave; ++i) {
     const int seg = wave + i * kWaves;
-    // (arguments go through locals: a template-dependent expression written
-    // straight into this builtin makes clang's host pass drop the kernel)
-    const int soff = kb * TL::kRowK;
-    lds_char* dst = lds + (buf * TL::kBytesK + seg * 1024);
     if (TL::kSegK % kWaves == 0 || seg < TL::kSegK)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsK, dst, 16, voffK[i], soff, 0, 0);
-  }
-#pragma unroll
-  for (int i = 0; i < TL::kSegVPerWave; ++i) {
-    const int seg = wave + i * kWaves;
-    const int soff = kb * TL::kRowV;
-    lds_char* dst = lds + (TL::kOffV + buf * TL::kBytesV + seg * 1024);
-    if (TL::kSegV % kWaves == 0 || seg < TL::kSegV)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsV, dst, 16, voffV[i], soff, 0, 0);
+      lds_load16(rsK, voffK[i], (uint32_t)kb * TL::kRowK, base + seg * 1024);
   }
   if constexpr (QK == QK_I8) {
-    const int nbS = n * 4;
-    const __amdgpu_buffer_rsrc_t rsS =
-        __builtin_amdgcn_make_buffer_rsrc((void*)sbase, (short)0, nbS, 0x00020000);
-    const int soff = kb * 4;
-    const uint32_t voff = lane * 4;
-    lds_char* dst = lds + (TL::kOffSk + buf * TL::kBytesSk);
-    if (wave == 0) __builtin_amdgcn_raw_ptr_buffer_load_lds(rsS, dst, 4, voff, soff, 0, 0);
+    if (wave == 0)
+      lds_load4(buffer_rsrc(sbase, (uint32_t)n * 4), (uint32_t)lane * 4, (uint32_t)kb * 4,
+                lds_address(smem) + TL::kOffSk + buf * TL::kBytesSk);
   }
 }
 
-// Two waves per SIMD (two workgroups per CU) where the LDS tiles allow it.
+// The same for V tile buffer `buf`.
 template <int D, int QK, int PV>
-constexpr int min_waves_per_simd() { return Tile<D, QK, PV>::kLds * 2 <= 160 * 1024 ? 2 : 1; }
+__device__ __forceinline__ void issue_v(char* smem, int wave, int kb, int buf, const void* vbase,
+                                        int n, const uint32_t* voffV) {
+  using TL = Tile<D, QK, PV>;
+  const i32x4 rsV = buffer_rsrc(vbase, (uint32_t)n * TL::kRowV);
+  const uint32_t base = lds_address(smem) + TL::kOffV + buf * TL::kBytesV;
+#pragma unroll
+  for (int i = 0; i < TL::kSegVPerWave; ++i) {
+    const int seg = wave + i * kWaves;
+    if (TL::kSegV % kWaves == 0 || seg < TL::kSegV)
+      lds_load16(rsV, voffV[i], (uint32_t)kb * TL::kRowV, base + seg * 1024);
+  }
+}
 
+// Workgroup barrier without the memory fence that __syncthreads() carries.
+// The fence would make every wave wait at the barrier for its in-flight
+// buffer->LDS loads, which are meant to overlap the following half-steps;
+// those loads are awaited explicitly (vmcnt) where the schedule needs them.
+// This wave's own LDS reads are drained first (lgkmcnt), and the asm's memory
+// clobber keeps the compiler from moving memory operations across it.
+__device__ __forceinline__ void block_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Schedule ("ping-pong").  Each key block j is split into two half-steps:
+//   M_j : the MFMA half-step  -- O^T += V_{j-1}^T P_{j-1}^T, then S_j = K_j Q^T
+//   X_j : the VALU half-step  -- mask, online max, exponentials, row sum,
+//                                rescale of O, P_j -> bf16
+// A wave runs M_0 X_0 M_1 X_1 ... M_n (the last M has only the P.V part).
+// The eight waves form two groups of four; group 1 runs one half-step
+// behind group 0, and every half-step ends at a workgroup barrier.  The two
+// waves sharing a SIMD therefore always run opposite half-steps: one keeps
+// the matrix cores busy while the other works the vector ALUs.
+// Buffers: K_j lives in K buffer j%2 and V_j in V buffer j%2.  At the start
+// of slot 2j the loads of K_{j+1} and V_j are issued (by every wave); they
+// are awaited at the end of slot 2j+1, so they land before slot 2j+2, the
+// first slot that reads them.  The buffers they overwrite were last read in
+// slot 2j-1.
 template <int D, int QK, int PV, bool CAUSAL, bool DEBUG_S>
-__global__ __launch_bounds__(kThreads, (min_waves_per_simd<D, QK, PV>()))
-void flash_fwd_kernel(FlashParams p) {
+__global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
   using QT = typename QKTraits<QK>::T;
   using VT = typename VTraits<PV>::T;
   using TL = Tile<D, QK, PV>;
@@ -178,6 +234,7 @@ void flash_fwd_kernel(FlashParams p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int group = wave >> 2;
   const int g = lane >> 5;
   const int n = lane & 31;
   const int N = p.n;
@@ -210,7 +267,13 @@ void flash_fwd_kernel(FlashParams p) {
       sq_log2 = qvalid ? p.q_scale[bh * N + qrow] * p.scale_log2 : 0.f;
   }
 
-  // ---- K/V block streaming: bounds-checked buffer loads straight into LDS
+  // Wait for the Q loads here, with a wait the compiler sees: otherwise its
+  // wait-count pass, unsure they finished before the loop, waits for all
+  // vector-memory traffic at their first use in every iteration, which would
+  // also drain the K/V prefetch.
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+
+  // ---- K/V streaming setup: per-lane source offsets of this wave's segments
   const void* kbase = (const char*)p.k + hoff * (int64_t)sizeof(QT);
   const void* vbase = (const char*)p.v + hoff * (int64_t)sizeof(VT);
   const void* sbase = (QK == QK_I8) ? (const void*)(p.k_scale + bh * N) : nullptr;
@@ -221,79 +284,126 @@ void flash_fwd_kernel(FlashParams p) {
 #pragma unroll
   for (int i = 0; i < TL::kSegVPerWave; ++i)
     voffV[i] = seg_src_offset(wave + i * kWaves, lane, TL::kRowV, TL::kStrV);
+
   const int kend = CAUSAL ? min(N, q0 + kBR) : N;
   const int nblk = (kend + kBC - 1) / kBC;
-  float m_run = -INFINITY;
+  // blocks at or after `nvis` lie entirely above this wave's causal diagonal
+  const int nvis = CAUSAL ? min(nblk, (q0w + 31) / kBC + 1) : nblk;
+
+  float m_run = -INFINITY;     // running max in log2 units
+  float mraw_run = -INFINITY;  // running max of the unscaled scores
   float l_run = 0.f;
   f32x16 oacc[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x16{};
+  float s[2][16];                                        // S_j, then P_j (fp32)
+  bf16x8 pb[PV == PV_BF16 ? 4 : 1];                      // P_j as the bf16 operand
+  float pf[PV == PV_BF16 ? 1 : 2][PV == PV_BF16 ? 1 : 16];  // P_j for the fp32 engines
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[ks][r] = 0.f;
 
   // per-lane LDS byte offsets of the operand reads (block-independent)
   const int k_lane = key_of_row(n) * TL::kStrK;
   const int v_lane = (8 * g + ((lane & 15) >> 2)) * TL::kStrV +
                      (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * (int)sizeof(VT);
 
-  issue_block<D, QK, PV>(smem, wave, lane, 0, 0, kbase, vbase, sbase, N, voffK, voffV);
-  for (int j = 0; j < nblk; ++j) {
-    const int kb = j * kBC;
-    const int buf = j & 1;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's loads of block j landed
-    __syncthreads();  // every wave's loads landed; every wave is done with block j-1
-    if (j + 1 < nblk)
-      issue_block<D, QK, PV>(smem, wave, lane, kb + kBC, buf ^ 1, kbase, vbase, sbase, N,
-                             voffK, voffV);
-    if (CAUSAL && kb > q0w + 31) continue;  // block entirely above this wave's diagonal
+  issue_k<D, QK, PV>(smem, wave, lane, 0, 0, kbase, sbase, N, voffK);
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  block_barrier();
 
-    const char* kt = (const char*)smem + buf * TL::kBytesK;
-    const char* vt = (const char*)smem + TL::kOffV + buf * TL::kBytesV;
-
-    // ---- S^T = K_j Q^T for two 32-key subtiles, in log2 units
-    float s[2][16];
+  // ---- the two half-steps, as lambdas shared by both groups' loops
+  auto half_m = [&](const int j) {
+    // ================= M_j: O^T += V_{j-1}^T P_{j-1}^T, then S_j = K_j Q^T
+    // (in this order the bf16 P registers die before the new scores are born)
+    if (j >= 1 && j - 1 < nvis) {
+      const char* vt = (const char*)smem + TL::kOffV + ((j - 1) & 1) * TL::kBytesV;
+      if constexpr (PV == PV_BF16) {
+        const char* vl = vt + v_lane;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const char* krow = kt + ks * 32 * TL::kStrK + k_lane;
-      if constexpr (QK == QK_BF16) {
-        f32x16 acc = {};
+        for (int u = 0; u < 4; ++u)
 #pragma unroll
-        for (int t = 0; t < QST; ++t) {
-          const i32x4 a = *(const i32x4*)(krow + 32 * t + 16 * g);
-          acc = mfma_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, qv[t]), acc);
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[ks][r] = acc[r] * p.scale_log2;
-      } else if constexpr (QK == QK_I8) {
-        i32x16 acc = {};
-#pragma unroll
-        for (int t = 0; t < QST; ++t) {
-          const i32x4 a = *(const i32x4*)(krow + 32 * t + 16 * g);
-          acc = mfma_i8(a, qv[t], acc);
-        }
-        if constexpr (DEBUG_S) {
-          if (qvalid) {
-            int32_t* dst = p.s_dbg + (bh * N + qrow) * (int64_t)N;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int key = kb + 32 * ks + key_of_reg(r, g);
-              if (key < N) dst[key] = acc[r];
-            }
+          for (int dt = 0; dt < DT; ++dt) {
+            const char* src = vl + 16 * u * TL::kStrV + 64 * dt;
+            const i16x4 lo = lds_read_tr16(src);
+            const i16x4 hi = lds_read_tr16(src + 4 * TL::kStrV);
+            oacc[dt] = mfma_bf16(join_bf16x8(lo, hi), pb[u], oacc[dt]);
           }
-        }
-        const float* skt = (const float*)(smem + TL::kOffSk + buf * TL::kBytesSk);
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          s[ks][r] = (float)acc[r] * (skt[32 * ks + key_of_reg(r, g)] * sq_log2);
       } else {
-        f32x16 acc = {};
 #pragma unroll
-        for (int t = 0; t < QST; ++t)
-          acc = mfma_f32(*(const float*)(krow + 4 * (2 * t + g)), qf[t], acc);
+        for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[ks][r] = acc[r] * p.scale_log2;
+          for (int r = 0; r < 16; ++r) {
+            const VT* vr = (const VT*)(vt + (32 * ks + key_of_reg(r, g)) * TL::kStrV) + n;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+              oacc[dt] = mfma_f32(to_f32<VT>(vr[32 * dt]), pf[ks][r], oacc[dt]);
+          }
       }
     }
-
-    // ---- causal diagonal and ragged tail: invisible keys score -inf
+    __builtin_amdgcn_sched_barrier(0);
+    if (j < nvis) {
+      const char* kt = (const char*)smem + (j & 1) * TL::kBytesK;
+      if constexpr (QK == QK_BF16) {
+        f32x16 acc0 = {}, acc1 = {};
+        const char* k0 = kt + k_lane + 16 * g;
+        const char* k1 = k0 + 32 * TL::kStrK;
+#pragma unroll
+        for (int st = 0; st < QST; ++st) {
+          const i32x4 a0 = *(const i32x4*)(k0 + 32 * st);
+          const i32x4 a1 = *(const i32x4*)(k1 + 32 * st);
+          acc0 = mfma_bf16(__builtin_bit_cast(bf16x8, a0), __builtin_bit_cast(bf16x8, qv[st]), acc0);
+          acc1 = mfma_bf16(__builtin_bit_cast(bf16x8, a1), __builtin_bit_cast(bf16x8, qv[st]), acc1);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          s[0][r] = acc0[r];  // raw q.k; scaled inside exp2
+          s[1][r] = acc1[r];
+        }
+      } else if constexpr (QK == QK_I8) {
+        const float* skt = (const float*)(smem + TL::kOffSk + (j & 1) * TL::kBytesSk);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const char* krow = kt + ks * 32 * TL::kStrK + k_lane + 16 * g;
+          i32x16 acc = {};
+#pragma unroll
+          for (int st = 0; st < QST; ++st)
+            acc = mfma_i8(*(const i32x4*)(krow + 32 * st), qv[st], acc);
+          if constexpr (DEBUG_S) {
+            if (qvalid) {
+              int32_t* dst = p.s_dbg + (bh * N + qrow) * (int64_t)N;
+#pragma unroll
+              for (int r = 0; r < 16; ++r) {
+                const int key = j * kBC + 32 * ks + key_of_reg(r, g);
+                if (key < N) dst[key] = acc[r];
+              }
+            }
+          }
+          // exact int32 -> fp32 (|acc| < 2^24), then the per-row scales
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            s[ks][r] = (float)acc[r] * (skt[32 * ks + key_of_reg(r, g)] * sq_log2);
+        }
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const char* krow = kt + ks * 32 * TL::kStrK + k_lane;
+          f32x16 acc = {};
+#pragma unroll
+          for (int st = 0; st < QST; ++st)
+            acc = mfma_f32(*(const float*)(krow + 4 * (2 * st + g)), qf[st], acc);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s[ks][r] = acc[r];
+        }
+      }
+    }
+  };
+  auto half_x = [&](const int j) {
+    if (j >= nvis) return;
+    // ================= X_j: online softmax of block j
+    const int kb = j * kBC;
+    // causal diagonal and ragged tail: invisible keys score -inf
     const bool need_mask = (kb + kBC > N) || (CAUSAL && kb + kBC - 1 > q0w);
     if (need_mask) {
 #pragma unroll
@@ -304,15 +414,19 @@ void flash_fwd_kernel(FlashParams p) {
           if (key >= N || (CAUSAL && key > qrow)) s[ks][r] = -INFINITY;
         }
     }
-
-    // ---- online softmax: running max, rescale factor, P, running sum
+    // bf16/fp32 Q,K: s holds raw dot products; the max is taken on them
+    // (the scale is positive) and P = exp2(fma(s, c, -m)) with
+    // m = c * max: one fma and one v_exp per score.  int8: s is already
+    // in log2 units (per-key scales), P = exp2(s - m).
     float mx = s[0][0];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[ks][r]);
     mx = pair32_max(mx);
-    const float m_new = fmaxf(m_run, mx);
+    const float mraw_new = fmaxf(mraw_run, mx);
+    mraw_run = mraw_new;
+    const float m_new = (QK == QK_I8) ? mraw_new : mraw_new * p.scale_log2;
     const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
     const float alpha = exp2_approx(m_run - m_use);
     m_run = m_new;
@@ -321,43 +435,59 @@ void flash_fwd_kernel(FlashParams p) {
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        s[ks][r] = exp2_approx(s[ks][r] - m_use);
+        if constexpr (QK == QK_I8)
+          s[ks][r] = exp2_approx(s[ks][r] - m_use);
+        else
+          s[ks][r] = exp2_approx(__builtin_fmaf(s[ks][r], p.scale_log2, -m_use));
         rs += s[ks][r];
       }
     l_run = l_run * alpha + rs;
-    if (__any(alpha != 1.f)) {
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
-    }
-
-    // ---- O^T += V_j^T P_j^T
+    for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
     if constexpr (PV == PV_BF16) {
-      bf16x8 pb[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u)
 #pragma unroll
         for (int e = 0; e < 8; ++e) pb[u][e] = (__bf16)s[u >> 1][8 * (u & 1) + e];
-      const char* vl = vt + v_lane;
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          const char* src = vl + 16 * u * TL::kStrV + 64 * dt;
-          const i16x4 lo = lds_read_tr16(src);
-          const i16x4 hi = lds_read_tr16(src + 4 * TL::kStrV);
-          oacc[dt] = mfma_bf16(join_bf16x8(lo, hi), pb[u], oacc[dt]);
-        }
     } else {
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float pv = p.p_round ? round_to_bf16(s[ks][r]) : s[ks][r];
-          const VT* vr = (const VT*)(vt + (32 * ks + key_of_reg(r, g)) * TL::kStrV) + n;
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt)
-            oacc[dt] = mfma_f32(to_f32<VT>(vr[32 * dt]), pv, oacc[dt]);
-        }
+        for (int r = 0; r < 16; ++r)
+          pf[ks][r] = p.p_round ? round_to_bf16(s[ks][r]) : s[ks][r];
+    }
+  };
+
+  // Group 0 runs slots (M_j, X_j) = (2j, 2j+1); group 1 runs (M_j, X_j) in
+  // slots (2j+1, 2j+2) after an idle slot 0.  Both loops pass exactly
+  // 2*nblk + 2 barriers, issue the loads of K_{j+1} and V_j at the start of
+  // slot 2j and await them at the end of slot 2j+1.
+  if (group == 0) {
+    for (int j = 0; j <= nblk; ++j) {
+      if (j + 1 < nblk)
+        issue_k<D, QK, PV>(smem, wave, lane, (j + 1) * kBC, (j + 1) & 1, kbase, sbase, N, voffK);
+      if (j < nblk) issue_v<D, QK, PV>(smem, wave, j * kBC, j & 1, vbase, N, voffV);
+      half_m(j);
+      block_barrier();
+      if (j < nblk) half_x(j);
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      block_barrier();
+    }
+  } else {
+    if (1 < nblk) issue_k<D, QK, PV>(smem, wave, lane, kBC, 1, kbase, sbase, N, voffK);
+    issue_v<D, QK, PV>(smem, wave, 0, 0, vbase, N, voffV);
+    block_barrier();
+    for (int j = 0; j <= nblk; ++j) {
+      half_m(j);
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      block_barrier();
+      if (j < nblk) {
+        if (j + 2 < nblk)
+          issue_k<D, QK, PV>(smem, wave, lane, (j + 2) * kBC, (j + 2) & 1, kbase, sbase, N, voffK);
+        if (j + 1 < nblk) issue_v<D, QK, PV>(smem, wave, (j + 1) * kBC, (j + 1) & 1, vbase, N, voffV);
+        half_x(j);
+        block_barrier();
+      }
     }
   }
 
