@@ -103,6 +103,22 @@ __device__ __forceinline__ int key_of_reg(int r, int g) {
   return 16 * (r >> 3) + 8 * g + (r & 7);
 }
 
+// Max of the 32 scores of a lane as a depth-4 tree of 3-input maxima.
+__device__ __forceinline__ float tree_max32(const float (&v)[2][16]) {
+  float a[11];
+#pragma unroll
+  for (int i = 0; i < 10; ++i) {
+    const int k0 = 3 * i, k1 = 3 * i + 1, k2 = 3 * i + 2;
+    a[i] = fmaxf(fmaxf(v[k0 >> 4][k0 & 15], v[k1 >> 4][k1 & 15]), v[k2 >> 4][k2 & 15]);
+  }
+  a[10] = fmaxf(v[1][14], v[1][15]);
+  const float b0 = fmaxf(fmaxf(a[0], a[1]), a[2]);
+  const float b1 = fmaxf(fmaxf(a[3], a[4]), a[5]);
+  const float b2 = fmaxf(fmaxf(a[6], a[7]), a[8]);
+  const float b3 = fmaxf(a[9], a[10]);
+  return fmaxf(fmaxf(fmaxf(b0, b1), b2), b3);
+}
+
 template <typename T> __device__ __forceinline__ float to_f32(T x);
 template <> __device__ __forceinline__ float to_f32<uint16_t>(uint16_t x) { return bf16_to_f32(x); }
 template <> __device__ __forceinline__ float to_f32<float>(float x) { return x; }
@@ -152,6 +168,10 @@ __device__ __forceinline__ void lds_load4(i32x4 rsrc, uint32_t voff, uint32_t so
       : "v"(voff), "s"(rsrc), "s"(soff), "s"(lds_addr)
       : "memory");
 }
+
+// Instruction classes for __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedMfma = 0x0008;
+constexpr int kSchedDsRead = 0x0100;
 
 // s_waitcnt immediate (gfx9 encoding) for vmcnt(0) with expcnt and lgkmcnt
 // left at their maxima: wait for this wave's outstanding vector-memory ops.
@@ -330,6 +350,11 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
             const i16x4 hi = lds_read_tr16(src + 4 * TL::kStrV);
             oacc[dt] = mfma_bf16(join_bf16x8(lo, hi), pb[u], oacc[dt]);
           }
+        // all LDS reads of the step first, then the matrix ops: the reads
+        // stream back while the first MFMAs run instead of each MFMA waiting
+        // on the latency of its own operand
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 8 * DT, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4 * DT, 0);
       } else {
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
@@ -356,6 +381,8 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
           acc0 = mfma_bf16(__builtin_bit_cast(bf16x8, a0), __builtin_bit_cast(bf16x8, qv[st]), acc0);
           acc1 = mfma_bf16(__builtin_bit_cast(bf16x8, a1), __builtin_bit_cast(bf16x8, qv[st]), acc1);
         }
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * QST, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2 * QST, 0);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           s[0][r] = acc0[r];  // raw q.k; scaled inside exp2
@@ -418,11 +445,7 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
     // (the scale is positive) and P = exp2(fma(s, c, -m)) with
     // m = c * max: one fma and one v_exp per score.  int8: s is already
     // in log2 units (per-key scales), P = exp2(s - m).
-    float mx = s[0][0];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[ks][r]);
+    float mx = tree_max32(s);
     mx = pair32_max(mx);
     const float mraw_new = fmaxf(mraw_run, mx);
     mraw_run = mraw_new;
@@ -430,7 +453,9 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
     const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
     const float alpha = exp2_approx(m_run - m_use);
     m_run = m_new;
-    float rs = 0.f;
+    // four independent partial row sums (a single += chain would serialise
+    // on the add latency)
+    float rsum[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
@@ -439,9 +464,9 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
           s[ks][r] = exp2_approx(s[ks][r] - m_use);
         else
           s[ks][r] = exp2_approx(__builtin_fmaf(s[ks][r], p.scale_log2, -m_use));
-        rs += s[ks][r];
+        rsum[r & 3] += s[ks][r];
       }
-    l_run = l_run * alpha + rs;
+    l_run = l_run * alpha + ((rsum[0] + rsum[1]) + (rsum[2] + rsum[3]));
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
     if constexpr (PV == PV_BF16) {
