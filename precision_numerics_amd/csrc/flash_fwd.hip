@@ -13,8 +13,15 @@
 // B_r, B_c; only rounding depends on them.
 //
 // Mapping onto CDNA4:
-//  * One workgroup = 4 wave64s = B_r = 128 query rows; each wave owns 32 rows.
-//    B_c = 64 keys per step, staged in LDS (K and V row-major, padded rows).
+//  * One workgroup = 8 wave64s = B_r = 256 query rows; each wave owns 32 rows.
+//    B_c = 64 keys per step, staged in LDS (K and V row-major, padded rows),
+//    double-buffered: the next block's K and V stream from HBM straight into
+//    LDS (buffer loads with the lds modifier) while the current one is used.
+//  * The eight waves form two groups of four, one wave of each group per
+//    SIMD.  The groups run half a step apart, so that while one wave of a
+//    SIMD issues its matrix products (P_{j-1} V_{j-1}, then S_j) the other
+//    does its softmax arithmetic (mask, max, exp, sums, rescale) on VALU:
+//    the two instruction streams overlap on each SIMD.
 //  * The wave computes S^T = K_j Q^T (32 keys x 32 queries per MFMA tile), so
 //    lane l owns query l%32 and half of the block's keys: the row max and row
 //    sum are in-lane reductions plus one permlane32_swap, and exp(m - m') is
