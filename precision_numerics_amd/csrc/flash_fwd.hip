@@ -14,14 +14,19 @@
 //
 // Mapping onto CDNA4:
 //  * One workgroup = 8 wave64s = B_r = 256 query rows; each wave owns 32 rows.
-//    B_c = 64 keys per step, staged in LDS (K and V row-major, padded rows),
-//    double-buffered: the next block's K and V stream from HBM straight into
-//    LDS (buffer loads with the lds modifier) while the current one is used.
+//    B_c = 128 keys per step (64 for the fp32 P*V engines, whose fp32 P
+//    operand needs twice the registers), staged in LDS (K and V row-major,
+//    padded rows), double-buffered: the next block's K and V stream from HBM
+//    straight into LDS (buffer loads with the lds modifier) while the current
+//    one is used.  The long block halves the per-key cost of the rescale of O,
+//    of the barriers and of the loop bookkeeping.
 //  * The eight waves form two groups of four, one wave of each group per
 //    SIMD.  The groups run half a step apart, so that while one wave of a
 //    SIMD issues its matrix products (P_{j-1} V_{j-1}, then S_j) the other
-//    does its softmax arithmetic (mask, max, exp, sums, rescale) on VALU:
-//    the two instruction streams overlap on each SIMD.
+//    does its softmax arithmetic (mask, max, exp, sums) on VALU: the two
+//    instruction streams overlap on each SIMD.  The rescale of O by
+//    exp(m - m') is issued in the matrix half-step, in the shadow of the
+//    P V products, which keeps the two half-steps closer in length.
 //  * The wave computes S^T = K_j Q^T (32 keys x 32 queries per MFMA tile), so
 //    lane l owns query l%32 and half of the block's keys: the row max and row
 //    sum are in-lane reductions plus one permlane32_swap, and exp(m - m') is
@@ -54,7 +59,11 @@ enum PVKind { PV_BF16 = 0, PV_F32_VBF16 = 1, PV_F32_VF32 = 2 };
 constexpr int kWaves = 8;            // two groups of four: one wave of each per SIMD
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBR = 32 * kWaves;     // query rows per workgroup
-constexpr int kBC = 64;              // keys per step
+
+// Keys per step: 128 when P enters P*V as bf16, 64 for the fp32 engines.
+template <int PV> struct BlockKeys { static constexpr int value = 128; };
+template <> struct BlockKeys<1> { static constexpr int value = 64; };
+template <> struct BlockKeys<2> { static constexpr int value = 64; };
 
 template <int QK> struct QKTraits;
 template <> struct QKTraits<QK_BF16> { using T = uint16_t; };
@@ -69,6 +78,7 @@ template <> struct VTraits<PV_F32_VF32> { using T = float; };
 // reads touch 4 rows x 64 bytes at a time).  Tiles are whole multiples of
 // 1 KiB, the footprint of one wave-wide 16-byte buffer load into LDS.
 template <int D, int QK, int PV> struct Tile {
+  static constexpr int kBC = BlockKeys<PV>::value;
   static constexpr int kRowK = D * (int)sizeof(typename QKTraits<QK>::T);
   static constexpr int kRowV = D * (int)sizeof(typename VTraits<PV>::T);
   static constexpr int kStrK = kRowK + 16;
@@ -110,20 +120,42 @@ __device__ __forceinline__ int key_of_reg(int r, int g) {
   return 16 * (r >> 3) + 8 * g + (r & 7);
 }
 
-// Max of the 32 scores of a lane as a depth-4 tree of 3-input maxima.
-__device__ __forceinline__ float tree_max32(const float (&v)[2][16]) {
-  float a[11];
+// Max of the N scores of a lane as a tree of 3-input maxima (v_max3_f32).
+template <int N>
+__device__ __forceinline__ float tree_max(const float (&x)[N]) {
+  if constexpr (N == 1) {
+    return x[0];
+  } else if constexpr (N == 2) {
+    return fmaxf(x[0], x[1]);
+  } else {
+    constexpr int M = (N + 2) / 3;
+    float y[M];
 #pragma unroll
-  for (int i = 0; i < 10; ++i) {
-    const int k0 = 3 * i, k1 = 3 * i + 1, k2 = 3 * i + 2;
-    a[i] = fmaxf(fmaxf(v[k0 >> 4][k0 & 15], v[k1 >> 4][k1 & 15]), v[k2 >> 4][k2 & 15]);
+    for (int i = 0; i < N / 3; ++i) y[i] = fmaxf(fmaxf(x[3 * i], x[3 * i + 1]), x[3 * i + 2]);
+    if constexpr (N % 3 == 1) y[M - 1] = x[N - 1];
+    if constexpr (N % 3 == 2) y[M - 1] = fmaxf(x[N - 2], x[N - 1]);
+    return tree_max<M>(y);
   }
-  a[10] = fmaxf(v[1][14], v[1][15]);
-  const float b0 = fmaxf(fmaxf(a[0], a[1]), a[2]);
-  const float b1 = fmaxf(fmaxf(a[3], a[4]), a[5]);
-  const float b2 = fmaxf(fmaxf(a[6], a[7]), a[8]);
-  const float b3 = fmaxf(a[9], a[10]);
-  return fmaxf(fmaxf(fmaxf(b0, b1), b2), b3);
+}
+
+template <bool B> struct BoolC { static constexpr bool value = B; };
+
+// Ends the live range of a register value: the result is unspecified and
+// costs no instruction.  Used where a path leaves a value the program never
+// reads again, so that the register allocator does not keep it alive across
+// the other paths that merge with it.
+template <typename T> __device__ __forceinline__ void forget(T& x) {
+  x = __builtin_nondeterministic_value(x);
+}
+
+// Pins a register value at this point of the program: the empty asm claims
+// to read and rewrite it, so the code producing the value cannot sink below
+// this point and its users cannot rise above it.  The workgroup barrier
+// orders memory operations only; without pins the compiler moves a
+// half-step's register arithmetic across it into the next slot, where the
+// wave would run it serially with its matrix products.
+template <typename T> __device__ __forceinline__ void pin(T& x) {
+  asm volatile("" : "+v"(x));
 }
 
 template <typename T> __device__ __forceinline__ float to_f32(T x);
@@ -157,23 +189,23 @@ __device__ __forceinline__ i32x4 buffer_rsrc(const void* base, uint32_t bytes) {
 // generated waits for other memory operations only become more conservative.
 __device__ __forceinline__ void lds_load16(i32x4 rsrc, uint32_t voff, uint32_t soff,
                                            uint32_t lds_addr) {
-  uint32_t saved;  // M0 is reserved by the compiler: save and restore it
+  // M0 carries the LDS destination; it is declared clobbered, so the compiler
+  // re-establishes any value of its own after the load
   asm volatile(
-      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %4\n\ts_nop 0\n\t"
-      "buffer_load_dwordx4 %1, %2, %3 offen lds\n\ts_mov_b32 m0, %0"
-      : "=&s"(saved)
+      "s_mov_b32 m0, %3\n\ts_nop 0\n\t"
+      "buffer_load_dwordx4 %0, %1, %2 offen lds"
+      :
       : "v"(voff), "s"(rsrc), "s"(soff), "s"(lds_addr)
-      : "memory");
+      : "memory", "m0");
 }
 __device__ __forceinline__ void lds_load4(i32x4 rsrc, uint32_t voff, uint32_t soff,
                                           uint32_t lds_addr) {
-  uint32_t saved;
   asm volatile(
-      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %4\n\ts_nop 0\n\t"
-      "buffer_load_dword %1, %2, %3 offen lds\n\ts_mov_b32 m0, %0"
-      : "=&s"(saved)
+      "s_mov_b32 m0, %3\n\ts_nop 0\n\t"
+      "buffer_load_dword %0, %1, %2 offen lds"
+      :
       : "v"(voff), "s"(rsrc), "s"(soff), "s"(lds_addr)
-      : "memory");
+      : "memory", "m0");
 }
 
 // Instruction classes for __builtin_amdgcn_sched_group_barrier.
@@ -183,6 +215,47 @@ constexpr int kSchedDsRead = 0x0100;
 // s_waitcnt immediate (gfx9 encoding) for vmcnt(0) with expcnt and lgkmcnt
 // left at their maxima: wait for this wave's outstanding vector-memory ops.
 constexpr int kWaitVmcnt0 = 0x0F70;
+
+// Wave priority (s_setprio) while a wave issues its matrix products.
+constexpr int kPrioMfma = 2;
+
+// Instruction-group orders for the matrix half-step (bf16 engines).  The
+// P.V products and the S products are scheduled as two separate regions: a
+// group mask names an instruction class, not an instruction, so in a shared
+// region the scheduler would fill the groups from whichever stream is ready.
+//
+// P.V region: per product two LDS reads, kAhead products ahead.
+template <int N, int I = 0>
+__device__ __forceinline__ void pv_schedule_step() {
+  constexpr int kAhead = 4;
+  if constexpr (I < N) {
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    if constexpr (I + kAhead < N) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+    pv_schedule_step<N, I + 1>();
+  }
+}
+template <int N>
+__device__ __forceinline__ void pv_schedule() {
+  constexpr int kAhead = 4;
+  __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * (N < kAhead ? N : kAhead), 0);
+  pv_schedule_step<N>();
+}
+// S region: one LDS read per product, kAhead products ahead.
+template <int N, int I = 0>
+__device__ __forceinline__ void s_schedule_step() {
+  constexpr int kAhead = 4;
+  if constexpr (I < N) {
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    if constexpr (I + kAhead < N) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+    s_schedule_step<N, I + 1>();
+  }
+}
+template <int N>
+__device__ __forceinline__ void s_schedule() {
+  constexpr int kAhead = 4;
+  __builtin_amdgcn_sched_group_barrier(kSchedDsRead, N < kAhead ? N : kAhead, 0);
+  s_schedule_step<N>();
+}
 
 __device__ __forceinline__ uint32_t lds_address(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
@@ -204,9 +277,13 @@ __device__ __forceinline__ void issue_k(char* smem, int wave, int lane, int kb, 
       lds_load16(rsK, voffK[i], (uint32_t)kb * TL::kRowK, base + seg * 1024);
   }
   if constexpr (QK == QK_I8) {
-    if (wave == 0)
-      lds_load4(buffer_rsrc(sbase, (uint32_t)n * 4), (uint32_t)lane * 4, (uint32_t)kb * 4,
-                lds_address(smem) + TL::kOffSk + buf * TL::kBytesSk);
+    if (wave == 0) {
+      const i32x4 rsS = buffer_rsrc(sbase, (uint32_t)n * 4);
+#pragma unroll
+      for (int h = 0; h < TL::kBC / 64; ++h)
+        lds_load4(rsS, (uint32_t)lane * 4, (uint32_t)(kb + 64 * h) * 4,
+                  lds_address(smem) + TL::kOffSk + buf * TL::kBytesSk + 256 * h);
+    }
   }
 }
 
@@ -254,7 +331,9 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
   using QT = typename QKTraits<QK>::T;
   using VT = typename VTraits<PV>::T;
   using TL = Tile<D, QK, PV>;
-  constexpr int DT = D / 32;  // 32-row d subtiles of O^T
+  constexpr int BC = TL::kBC;
+  constexpr int NKS = BC / 32;  // 32-key subtiles of S^T per block
+  constexpr int DT = D / 32;    // 32-row d subtiles of O^T
 
   __shared__ __attribute__((aligned(1024))) char smem[TL::kLds];
 
@@ -313,9 +392,12 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
     voffV[i] = seg_src_offset(wave + i * kWaves, lane, TL::kRowV, TL::kStrV);
 
   const int kend = CAUSAL ? min(N, q0 + kBR) : N;
-  const int nblk = (kend + kBC - 1) / kBC;
-  // blocks at or after `nvis` lie entirely above this wave's causal diagonal
-  const int nvis = CAUSAL ? min(nblk, (q0w + 31) / kBC + 1) : nblk;
+  const int nblk = (kend + BC - 1) / BC;
+  // Every wave runs all nblk blocks of its workgroup.  Near the causal
+  // diagonal a block can lie entirely above a wave's rows: its scores are all
+  // masked, so m and l are unchanged (exp(m - m') = 1) and P = 0 adds
+  // nothing to O.  Running it keeps the loop free of per-wave conditions,
+  // whose merging paths would keep dead score registers alive.
 
   float m_run = -INFINITY;     // running max in log2 units
   float mraw_run = -INFINITY;  // running max of the unscaled scores
@@ -323,11 +405,11 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
   f32x16 oacc[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x16{};
-  float s[2][16];                                        // S_j, then P_j (fp32)
-  bf16x8 pb[PV == PV_BF16 ? 4 : 1];                      // P_j as the bf16 operand
-  float pf[PV == PV_BF16 ? 1 : 2][PV == PV_BF16 ? 1 : 16];  // P_j for the fp32 engines
+  float s[NKS][16];                                          // S_j, then P_j (fp32)
+  bf16x8 pb[PV == PV_BF16 ? BC / 16 : 1];                    // P_j as the bf16 operand
+  float pf[PV == PV_BF16 ? 1 : NKS][PV == PV_BF16 ? 1 : 16];  // P_j for the fp32 engines
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks)
+  for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[ks][r] = 0.f;
 
@@ -340,108 +422,242 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   block_barrier();
 
-  // ---- the two half-steps, as lambdas shared by both groups' loops
-  auto half_m = [&](const int j) {
-    // ================= M_j: O^T += V_{j-1}^T P_{j-1}^T, then S_j = K_j Q^T
-    // (in this order the bf16 P registers die before the new scores are born)
-    if (j >= 1 && j - 1 < nvis) {
-      const char* vt = (const char*)smem + TL::kOffV + ((j - 1) & 1) * TL::kBytesV;
-      if constexpr (PV == PV_BF16) {
-        const char* vl = vt + v_lane;
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt) {
-            const char* src = vl + 16 * u * TL::kStrV + 64 * dt;
-            const i16x4 lo = lds_read_tr16(src);
-            const i16x4 hi = lds_read_tr16(src + 4 * TL::kStrV);
-            oacc[dt] = mfma_bf16(join_bf16x8(lo, hi), pb[u], oacc[dt]);
-          }
-        // all LDS reads of the step first, then the matrix ops: the reads
-        // stream back while the first MFMAs run instead of each MFMA waiting
-        // on the latency of its own operand
-        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 8 * DT, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4 * DT, 0);
-      } else {
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const VT* vr = (const VT*)(vt + (32 * ks + key_of_reg(r, g)) * TL::kStrV) + n;
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt)
-              oacc[dt] = mfma_f32(to_f32<VT>(vr[32 * dt]), pf[ks][r], oacc[dt]);
-          }
-      }
+  // ================= M_j: O^T += V_{j-1}^T P_{j-1}^T, then S_j = K_j Q^T
+  // (in this order the P_{j-1} registers die before the new scores are born).
+  // DO_PV / DO_S select the parts at compile time, so that the steady-state
+  // step is one straight-line region the scheduler can interleave: LDS reads
+  // run a few matrix products ahead of their use, and the rescale of O is
+  // spread over the products of the preceding d subtile.
+  // Loads a matrix half-step issues for the next tiles (workgroup group 0):
+  // K rows kb_k.. into K buffer buf_k if k_on, V rows kb_v.. into V buffer
+  // buf_v if v_on.
+  struct Prefetch {
+    int kb_k, buf_k, kb_v, buf_v;
+    bool k_on, v_on;
+  };
+  const i32x4 rsK = buffer_rsrc(kbase, (uint32_t)N * TL::kRowK);
+  const i32x4 rsV = buffer_rsrc(vbase, (uint32_t)N * TL::kRowV);
+  constexpr int NSEG = TL::kSegKPerWave + TL::kSegVPerWave;
+  // this wave's segment q of the request: K segments first, then V
+  auto issue_one = [&](const int q, const Prefetch& rq) __attribute__((always_inline)) {
+    if (q < TL::kSegKPerWave) {
+      const int seg = wave + q * kWaves;
+      if (rq.k_on && (TL::kSegK % kWaves == 0 || seg < TL::kSegK))
+        lds_load16(rsK, voffK[q], (uint32_t)rq.kb_k * TL::kRowK,
+                   lds_address(smem) + rq.buf_k * TL::kBytesK + seg * 1024);
+    } else {
+      const int qv_ = q - TL::kSegKPerWave;
+      const int seg = wave + qv_ * kWaves;
+      if (rq.v_on && (TL::kSegV % kWaves == 0 || seg < TL::kSegV))
+        lds_load16(rsV, voffV[qv_], (uint32_t)rq.kb_v * TL::kRowV,
+                   lds_address(smem) + TL::kOffV + rq.buf_v * TL::kBytesV + seg * 1024);
     }
-    __builtin_amdgcn_sched_barrier(0);
-    if (j < nvis) {
-      const char* kt = (const char*)smem + (j & 1) * TL::kBytesK;
-      if constexpr (QK == QK_BF16) {
-        f32x16 acc0 = {}, acc1 = {};
-        const char* k0 = kt + k_lane + 16 * g;
-        const char* k1 = k0 + 32 * TL::kStrK;
+  };
+
+  auto m_body = [&](const int j, auto do_pv_c, auto do_s_c, auto issue_c,
+                    const Prefetch& rq) __attribute__((always_inline)) {
+    constexpr bool DO_PV = decltype(do_pv_c)::value;
+    constexpr bool DO_S = decltype(do_s_c)::value;
+    constexpr bool ISSUE = decltype(issue_c)::value;
+    if constexpr (PV == PV_BF16 && QK == QK_BF16) {
+      // The whole half-step in program order, fenced so that the scheduler
+      // keeps it: product i is followed by the LDS reads of product
+      // i + kAhead, so every operand is requested kAhead products (about
+      // kAhead * 32 cycles, more than the LDS latency) before its use, also
+      // across the switch from the P.V products to the S products.  The
+      // loads of the next tiles are spread over the products.  No VALU
+      // instruction sits in this stream: the wave sharing the SIMD runs a
+      // dense VALU stream meanwhile, and an in-order wave whose VALU
+      // instruction waits for the VALU port also holds back the products
+      // behind it.
+      constexpr int kAhead = 8;
+      constexpr int NPV = DO_PV ? DT * (BC / 16) : 0;  // P.V products, u-major
+      constexpr int NSM = DO_S ? NKS * QST : 0;        // S products, chain by chain
+      const char* vl = (const char*)smem + TL::kOffV + ((j - 1) & 1) * TL::kBytesV + v_lane;
+      const char* k0 = (const char*)smem + (j & 1) * TL::kBytesK + k_lane + 16 * g;
+      i16x4 vlo[NPV > 0 ? NPV : 1], vhi[NPV > 0 ? NPV : 1];
+      i32x4 kf[NSM > 0 ? NSM : 1];
+      f32x16 acc[NKS];
 #pragma unroll
-        for (int st = 0; st < QST; ++st) {
-          const i32x4 a0 = *(const i32x4*)(k0 + 32 * st);
-          const i32x4 a1 = *(const i32x4*)(k1 + 32 * st);
-          acc0 = mfma_bf16(__builtin_bit_cast(bf16x8, a0), __builtin_bit_cast(bf16x8, qv[st]), acc0);
-          acc1 = mfma_bf16(__builtin_bit_cast(bf16x8, a1), __builtin_bit_cast(bf16x8, qv[st]), acc1);
+      for (int ks = 0; ks < NKS; ++ks) acc[ks] = f32x16{};
+      auto load = [&](const int i) __attribute__((always_inline)) {
+        if (i < NPV) {
+          const char* src = vl + 16 * (i / DT) * TL::kStrV + 64 * (i % DT);
+          vlo[i] = lds_read_tr16(src);
+          vhi[i] = lds_read_tr16(src + 4 * TL::kStrV);
+        } else {
+          const int t = i - NPV;
+          kf[t] = *(const i32x4*)(k0 + (t / QST) * 32 * TL::kStrK + 32 * (t % QST));
         }
-        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * QST, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2 * QST, 0);
+      };
+      auto product = [&](const int i) __attribute__((always_inline)) {
+        if (i < NPV) {
+          oacc[i % DT] = mfma_bf16(join_bf16x8(vlo[i], vhi[i]), pb[i / DT], oacc[i % DT]);
+        } else {
+          const int t = i - NPV;
+          acc[t / QST] = mfma_bf16(__builtin_bit_cast(bf16x8, kf[t]),
+                                   __builtin_bit_cast(bf16x8, qv[t % QST]), acc[t / QST]);
+        }
+      };
+      // The wave sharing this SIMD runs its softmax meanwhile; a dense VALU
+      // stream would win the issue arbitration against the products, so
+      // this wave raises its priority for the products and drops it after.
+      __builtin_amdgcn_s_setprio(kPrioMfma);
+#pragma unroll
+      for (int i = 0; i < kAhead && i < NPV + NSM; ++i) load(i);
+#pragma unroll
+      for (int i = 0; i < NPV + NSM; ++i) {
+        __builtin_amdgcn_sched_barrier(0);
+        product(i);
+        if (i + kAhead < NPV + NSM) load(i + kAhead);
+        if constexpr (ISSUE) {
+#pragma unroll
+          for (int q = 0; q < NSEG; ++q)
+            if ((2 * q + 1) * (NPV + NSM) / (2 * NSEG) == i) issue_one(q, rq);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(0);
+      if constexpr (DO_S) {
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) pin(acc[ks]);
+      }
+      if constexpr (DO_PV) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) pin(oacc[dt]);
+      }
+#pragma unroll
+      for (int u = 0; u < BC / 16; ++u) forget(pb[u]);
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          s[0][r] = acc0[r];  // raw q.k; scaled inside exp2
-          s[1][r] = acc1[r];
+          if constexpr (DO_S) s[ks][r] = acc[ks][r];  // raw q.k; scaled inside exp2
+          else forget(s[ks][r]);
         }
-      } else if constexpr (QK == QK_I8) {
-        const float* skt = (const float*)(smem + TL::kOffSk + (j & 1) * TL::kBytesSk);
+    } else {
+      if constexpr (ISSUE) {
+        if (rq.k_on)
+          issue_k<D, QK, PV>(smem, wave, lane, rq.kb_k, rq.buf_k, kbase, sbase, N, voffK);
+        if (rq.v_on) issue_v<D, QK, PV>(smem, wave, rq.kb_v, rq.buf_v, vbase, N, voffV);
+      }
+      if constexpr (DO_PV) {
+        const char* vt = (const char*)smem + TL::kOffV + ((j - 1) & 1) * TL::kBytesV;
+        if constexpr (PV == PV_BF16) {
+          // key-group-outer order: P_{j-1} registers die group by group, so
+          // they are gone before the new scores are born
+          const char* vl = vt + v_lane;
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const char* krow = kt + ks * 32 * TL::kStrK + k_lane + 16 * g;
-          i32x16 acc = {};
+          for (int u = 0; u < BC / 16; ++u)
 #pragma unroll
-          for (int st = 0; st < QST; ++st)
-            acc = mfma_i8(*(const i32x4*)(krow + 32 * st), qv[st], acc);
-          if constexpr (DEBUG_S) {
-            if (qvalid) {
-              int32_t* dst = p.s_dbg + (bh * N + qrow) * (int64_t)N;
-#pragma unroll
-              for (int r = 0; r < 16; ++r) {
-                const int key = j * kBC + 32 * ks + key_of_reg(r, g);
-                if (key < N) dst[key] = acc[r];
-              }
+            for (int dt = 0; dt < DT; ++dt) {
+              const char* src = vl + 16 * u * TL::kStrV + 64 * dt;
+              const i16x4 lo = lds_read_tr16(src);
+              const i16x4 hi = lds_read_tr16(src + 4 * TL::kStrV);
+              oacc[dt] = mfma_bf16(join_bf16x8(lo, hi), pb[u], oacc[dt]);
             }
-          }
-          // exact int32 -> fp32 (|acc| < 2^24), then the per-row scales
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            s[ks][r] = (float)acc[r] * (skt[32 * ks + key_of_reg(r, g)] * sq_log2);
+          for (int u = 0; u < BC / 16; ++u) forget(pb[u]);
+          pv_schedule<DT * (BC / 16)>();
+          __builtin_amdgcn_sched_barrier(0);
+        } else {
+#pragma unroll
+          for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const VT* vr = (const VT*)(vt + (32 * ks + key_of_reg(r, g)) * TL::kStrV) + n;
+#pragma unroll
+              for (int dt = 0; dt < DT; ++dt)
+                oacc[dt] = mfma_f32(to_f32<VT>(vr[32 * dt]), pf[ks][r], oacc[dt]);
+            }
+#pragma unroll
+          for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) forget(pf[ks][r]);
         }
       } else {
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const char* krow = kt + ks * 32 * TL::kStrK + k_lane;
-          f32x16 acc = {};
+        for (int u = 0; u < (PV == PV_BF16 ? BC / 16 : 1); ++u) forget(pb[u]);
 #pragma unroll
-          for (int st = 0; st < QST; ++st)
-            acc = mfma_f32(*(const float*)(krow + 4 * (2 * st + g)), qf[st], acc);
+        for (int ks = 0; ks < (PV == PV_BF16 ? 1 : NKS); ++ks)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) s[ks][r] = acc[r];
+          for (int r = 0; r < (PV == PV_BF16 ? 1 : 16); ++r) forget(pf[ks][r]);
+      }
+      if constexpr (!DO_S) {
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) forget(s[ks][r]);
+      }
+      if constexpr (DO_S) {
+        const char* kt = (const char*)smem + (j & 1) * TL::kBytesK;
+        if constexpr (QK == QK_BF16) {
+          f32x16 acc[NKS];
+#pragma unroll
+          for (int ks = 0; ks < NKS; ++ks) acc[ks] = f32x16{};
+          // one accumulator chain at a time (back-to-back dependent products
+          // issue at full rate), so that the score registers fill up gradually
+          const char* k0 = kt + k_lane + 16 * g;
+#pragma unroll
+          for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+            for (int st = 0; st < QST; ++st) {
+              const i32x4 a = *(const i32x4*)(k0 + ks * 32 * TL::kStrK + 32 * st);
+              acc[ks] = mfma_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, qv[st]),
+                                  acc[ks]);
+            }
+          s_schedule<NKS * QST>();
+#pragma unroll
+          for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[ks][r] = acc[ks][r];  // raw q.k; scaled inside exp2
+        } else if constexpr (QK == QK_I8) {
+          const float* skt = (const float*)(smem + TL::kOffSk + (j & 1) * TL::kBytesSk);
+#pragma unroll
+          for (int ks = 0; ks < NKS; ++ks) {
+            const char* krow = kt + ks * 32 * TL::kStrK + k_lane + 16 * g;
+            i32x16 acc = {};
+#pragma unroll
+            for (int st = 0; st < QST; ++st)
+              acc = mfma_i8(*(const i32x4*)(krow + 32 * st), qv[st], acc);
+            if constexpr (DEBUG_S) {
+              if (qvalid) {
+                int32_t* dst = p.s_dbg + (bh * N + qrow) * (int64_t)N;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                  const int key = j * BC + 32 * ks + key_of_reg(r, g);
+                  if (key < N) dst[key] = acc[r];
+                }
+              }
+            }
+            // exact int32 -> fp32 (|acc| < 2^24), then the per-row scales
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              s[ks][r] = (float)acc[r] * (skt[32 * ks + key_of_reg(r, g)] * sq_log2);
+          }
+        } else {
+#pragma unroll
+          for (int ks = 0; ks < NKS; ++ks) {
+            const char* krow = kt + ks * 32 * TL::kStrK + k_lane;
+            f32x16 acc = {};
+#pragma unroll
+            for (int st = 0; st < QST; ++st)
+              acc = mfma_f32(*(const float*)(krow + 4 * (2 * st + g)), qf[st], acc);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[ks][r] = acc[r];
+          }
         }
       }
     }
   };
-  auto half_x = [&](const int j) {
-    if (j >= nvis) return;
-    // ================= X_j: online softmax of block j
-    const int kb = j * kBC;
+  // ================= X_j: online softmax of block j
+  auto half_x = [&](const int j) __attribute__((always_inline)) {
+    const int kb = j * BC;
     // causal diagonal and ragged tail: invisible keys score -inf
-    const bool need_mask = (kb + kBC > N) || (CAUSAL && kb + kBC - 1 > q0w);
+    const bool need_mask = (kb + BC > N) || (CAUSAL && kb + BC - 1 > q0w);
     if (need_mask) {
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
+      for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = kb + 32 * ks + key_of_reg(r, g);
@@ -452,7 +668,10 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
     // (the scale is positive) and P = exp2(fma(s, c, -m)) with
     // m = c * max: one fma and one v_exp per score.  int8: s is already
     // in log2 units (per-key scales), P = exp2(s - m).
-    float mx = tree_max32(s);
+    float flat[NKS * 16];
+#pragma unroll
+    for (int i = 0; i < NKS * 16; ++i) flat[i] = s[i / 16][i % 16];
+    float mx = tree_max(flat);
     mx = pair32_max(mx);
     const float mraw_new = fmaxf(mraw_run, mx);
     mraw_run = mraw_new;
@@ -464,7 +683,7 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
     // on the add latency)
     float rsum[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
+    for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         if constexpr (QK == QK_I8)
@@ -478,49 +697,81 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
     for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
     if constexpr (PV == PV_BF16) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+      for (int u = 0; u < BC / 16; ++u)
 #pragma unroll
         for (int e = 0; e < 8; ++e) pb[u][e] = (__bf16)s[u >> 1][8 * (u & 1) + e];
+#pragma unroll
+      for (int u = 0; u < BC / 16; ++u) pin(pb[u]);
     } else {
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
+      for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
+        for (int r = 0; r < 16; ++r) {
           pf[ks][r] = p.p_round ? round_to_bf16(s[ks][r]) : s[ks][r];
+          pin(pf[ks][r]);
+        }
     }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) pin(oacc[dt]);
+    pin(l_run);
+    pin(m_run);
+    pin(mraw_run);
   };
 
   // Group 0 runs slots (M_j, X_j) = (2j, 2j+1); group 1 runs (M_j, X_j) in
-  // slots (2j+1, 2j+2) after an idle slot 0.  Both loops pass exactly
-  // 2*nblk + 2 barriers, issue the loads of K_{j+1} and V_j at the start of
-  // slot 2j and await them at the end of slot 2j+1.
+  // slots (2j+1, 2j+2) after an idle slot 0.  Both pass exactly 2*nblk + 2
+  // barriers, issue the loads of K_{j+1} and V_j at the start of slot 2j and
+  // await them at the end of slot 2j+1.  M_0 has no P.V part and M_nblk no
+  // S part; they are peeled off the loop, whose body is the full step.
+  constexpr BoolC<true> kYes{};
+  constexpr BoolC<false> kNo{};
+  const Prefetch kNone{0, 0, 0, 0, false, false};
   if (group == 0) {
-    for (int j = 0; j <= nblk; ++j) {
-      if (j + 1 < nblk)
-        issue_k<D, QK, PV>(smem, wave, lane, (j + 1) * kBC, (j + 1) & 1, kbase, sbase, N, voffK);
-      if (j < nblk) issue_v<D, QK, PV>(smem, wave, j * kBC, j & 1, vbase, N, voffV);
-      half_m(j);
+    // slots 0, 1 (M_0 issues K_1 and V_0)
+    m_body(0, kNo, kYes, kYes, Prefetch{BC, 1, 0, 0, 1 < nblk, true});
+    block_barrier();
+    half_x(0);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    block_barrier();
+    for (int j = 1; j < nblk; ++j) {
+      // slots 2j, 2j+1 (M_j issues K_{j+1} and V_j)
+      m_body(j, kYes, kYes, kYes, Prefetch{(j + 1) * BC, (j + 1) & 1, j * BC, j & 1, j + 1 < nblk, true});
       block_barrier();
-      if (j < nblk) half_x(j);
+      half_x(j);
       __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
       block_barrier();
     }
+    // slots 2 nblk, 2 nblk + 1
+    m_body(nblk, kYes, kNo, kNo, kNone);
+    block_barrier();
+    block_barrier();
   } else {
-    if (1 < nblk) issue_k<D, QK, PV>(smem, wave, lane, kBC, 1, kbase, sbase, N, voffK);
+    // slot 0
+    if (1 < nblk) issue_k<D, QK, PV>(smem, wave, lane, BC, 1, kbase, sbase, N, voffK);
     issue_v<D, QK, PV>(smem, wave, 0, 0, vbase, N, voffV);
     block_barrier();
-    for (int j = 0; j <= nblk; ++j) {
-      half_m(j);
+    // slots 1, 2
+    m_body(0, kNo, kYes, kNo, kNone);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    block_barrier();
+    if (2 < nblk) issue_k<D, QK, PV>(smem, wave, lane, 2 * BC, 0, kbase, sbase, N, voffK);
+    if (1 < nblk) issue_v<D, QK, PV>(smem, wave, BC, 1, vbase, N, voffV);
+    half_x(0);
+    block_barrier();
+    for (int j = 1; j < nblk; ++j) {
+      // slots 2j+1, 2j+2
+      m_body(j, kYes, kYes, kNo, kNone);
       __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
       block_barrier();
-      if (j < nblk) {
-        if (j + 2 < nblk)
-          issue_k<D, QK, PV>(smem, wave, lane, (j + 2) * kBC, (j + 2) & 1, kbase, sbase, N, voffK);
-        if (j + 1 < nblk) issue_v<D, QK, PV>(smem, wave, (j + 1) * kBC, (j + 1) & 1, vbase, N, voffV);
-        half_x(j);
-        block_barrier();
-      }
+      if (j + 2 < nblk)
+        issue_k<D, QK, PV>(smem, wave, lane, (j + 2) * BC, (j + 2) & 1, kbase, sbase, N, voffK);
+      if (j + 1 < nblk) issue_v<D, QK, PV>(smem, wave, (j + 1) * BC, (j + 1) & 1, vbase, N, voffV);
+      half_x(j);
+      block_barrier();
     }
+    // slot 2 nblk + 1
+    m_body(nblk, kYes, kNo, kNo, kNone);
+    block_barrier();
   }
 
   // ---- epilogue: O = O^T / l, stored row-major; optional log-sum-exp
