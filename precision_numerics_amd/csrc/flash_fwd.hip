@@ -87,8 +87,11 @@ template <int D, int QK, int PV> struct Tile {
   static constexpr int kBytesV = kBC * kStrV;
   static constexpr int kSegK = kBytesK / 1024;
   static constexpr int kSegV = kBytesV / 1024;
-  static constexpr int kSegKPerWave = (kSegK + kWaves - 1) / kWaves;
-  static constexpr int kSegVPerWave = (kSegV + kWaves - 1) / kWaves;
+  // the four waves of group 0 issue the K tiles, those of group 1 the V tiles
+  static constexpr int kIssuers = kWaves / 2;
+  static constexpr int kSegKPerWave = (kSegK + kIssuers - 1) / kIssuers;
+  static constexpr int kSegVPerWave = (kSegV + kIssuers - 1) / kIssuers;
+  static constexpr int kSegPerWave = kSegKPerWave > kSegVPerWave ? kSegKPerWave : kSegVPerWave;
   static constexpr int kBytesSk = (QK == QK_I8) ? kBC * 4 : 0;
   // [K buf0][K buf1][V buf0][V buf1][sk buf0][sk buf1]
   static constexpr int kOffV = 2 * kBytesK;
@@ -261,10 +264,11 @@ __device__ __forceinline__ uint32_t lds_address(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
 }
 
-// Issue this wave's share of the loads that fill K tile buffer `buf` with
-// key rows kb..kb+63 (and, for int8, the 64 key scales).  Asynchronous.
+// Issue this wave's share (w = 0..3 inside the issuing group) of the loads
+// that fill K tile buffer `buf` with key rows kb.. (and, for int8, the key
+// scales).  Asynchronous.
 template <int D, int QK, int PV>
-__device__ __forceinline__ void issue_k(char* smem, int wave, int lane, int kb, int buf,
+__device__ __forceinline__ void issue_k(char* smem, int w, int lane, int kb, int buf,
                                         const void* kbase, const void* sbase, int n,
                                         const uint32_t* voffK) {
   using TL = Tile<D, QK, PV>;
@@ -272,12 +276,12 @@ __device__ __forceinline__ void issue_k(char* smem, int wave, int lane, int kb, 
   const uint32_t base = lds_address(smem) + buf * TL::kBytesK;
 #pragma unroll
   for (int i = 0; i < TL::kSegKPerWave; ++i) {
-    const int seg = wave + i * kWaves;
-    if (TL::kSegK % kWaves == 0 || seg < TL::kSegK)
+    const int seg = w + i * TL::kIssuers;
+    if (TL::kSegK % TL::kIssuers == 0 || seg < TL::kSegK)
       lds_load16(rsK, voffK[i], (uint32_t)kb * TL::kRowK, base + seg * 1024);
   }
   if constexpr (QK == QK_I8) {
-    if (wave == 0) {
+    if (w == 0) {
       const i32x4 rsS = buffer_rsrc(sbase, (uint32_t)n * 4);
 #pragma unroll
       for (int h = 0; h < TL::kBC / 64; ++h)
@@ -287,17 +291,17 @@ __device__ __forceinline__ void issue_k(char* smem, int wave, int lane, int kb, 
   }
 }
 
-// The same for V tile buffer `buf`.
+// The same for V tile buffer `buf` (issued by group 1).
 template <int D, int QK, int PV>
-__device__ __forceinline__ void issue_v(char* smem, int wave, int kb, int buf, const void* vbase,
+__device__ __forceinline__ void issue_v(char* smem, int w, int kb, int buf, const void* vbase,
                                         int n, const uint32_t* voffV) {
   using TL = Tile<D, QK, PV>;
   const i32x4 rsV = buffer_rsrc(vbase, (uint32_t)n * TL::kRowV);
   const uint32_t base = lds_address(smem) + TL::kOffV + buf * TL::kBytesV;
 #pragma unroll
   for (int i = 0; i < TL::kSegVPerWave; ++i) {
-    const int seg = wave + i * kWaves;
-    if (TL::kSegV % kWaves == 0 || seg < TL::kSegV)
+    const int seg = w + i * TL::kIssuers;
+    if (TL::kSegV % TL::kIssuers == 0 || seg < TL::kSegV)
       lds_load16(rsV, voffV[i], (uint32_t)kb * TL::kRowV, base + seg * 1024);
   }
 }
@@ -353,6 +357,23 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
   const int64_t hoff = bh * (int64_t)N * D;
   const QT* Qg = (const QT*)p.q + hoff;
 
+  // ---- K/V streaming setup: per-lane source offsets of this wave's segments
+  const void* kbase = (const char*)p.k + hoff * (int64_t)sizeof(QT);
+  const void* vbase = (const char*)p.v + hoff * (int64_t)sizeof(VT);
+  const void* sbase = (QK == QK_I8) ? (const void*)(p.k_scale + bh * N) : nullptr;
+  // group 0 holds the source offsets of its K segments, group 1 those of
+  // its V segments, in the same registers
+  const int wg = wave & (TL::kIssuers - 1);  // wave index inside its group
+  uint32_t voff[TL::kSegPerWave];
+#pragma unroll
+  for (int i = 0; i < TL::kSegPerWave; ++i)
+    voff[i] = group == 0 ? seg_src_offset(wg + i * TL::kIssuers, lane, TL::kRowK, TL::kStrK)
+                         : seg_src_offset(wg + i * TL::kIssuers, lane, TL::kRowV, TL::kStrV);
+
+
+  // The first K tile streams in while this lane's Q row loads.
+  if (group == 0) issue_k<D, QK, PV>(smem, wg, lane, 0, 0, kbase, sbase, N, voff);
+
   // ---- this lane's query row as the B operand of S^T = K Q^T (registers)
   constexpr int QST = (QK == QK_BF16) ? D / 16 : (QK == QK_I8 ? D / 32 : D / 2);
   i32x4 qv[QK == QK_F32 ? 1 : QST];
@@ -373,23 +394,11 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
       sq_log2 = qvalid ? p.q_scale[bh * N + qrow] * p.scale_log2 : 0.f;
   }
 
-  // Wait for the Q loads here, with a wait the compiler sees: otherwise its
-  // wait-count pass, unsure they finished before the loop, waits for all
-  // vector-memory traffic at their first use in every iteration, which would
-  // also drain the K/V prefetch.
+  // One wait for the Q row and the first K tile, with a wait the compiler
+  // sees: otherwise its wait-count pass, unsure the Q loads finished before
+  // the loop, waits for all vector-memory traffic at their first use in
+  // every iteration, which would also drain the K/V prefetch.
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-
-  // ---- K/V streaming setup: per-lane source offsets of this wave's segments
-  const void* kbase = (const char*)p.k + hoff * (int64_t)sizeof(QT);
-  const void* vbase = (const char*)p.v + hoff * (int64_t)sizeof(VT);
-  const void* sbase = (QK == QK_I8) ? (const void*)(p.k_scale + bh * N) : nullptr;
-  uint32_t voffK[TL::kSegKPerWave], voffV[TL::kSegVPerWave];
-#pragma unroll
-  for (int i = 0; i < TL::kSegKPerWave; ++i)
-    voffK[i] = seg_src_offset(wave + i * kWaves, lane, TL::kRowK, TL::kStrK);
-#pragma unroll
-  for (int i = 0; i < TL::kSegVPerWave; ++i)
-    voffV[i] = seg_src_offset(wave + i * kWaves, lane, TL::kRowV, TL::kStrV);
 
   const int kend = CAUSAL ? min(N, q0 + kBR) : N;
   const int nblk = (kend + BC - 1) / BC;
@@ -418,8 +427,6 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
   const int v_lane = (8 * g + ((lane & 15) >> 2)) * TL::kStrV +
                      (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * (int)sizeof(VT);
 
-  issue_k<D, QK, PV>(smem, wave, lane, 0, 0, kbase, sbase, N, voffK);
-  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   block_barrier();
 
   // ================= M_j: O^T += V_{j-1}^T P_{j-1}^T, then S_j = K_j Q^T
@@ -428,30 +435,20 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
   // step is one straight-line region the scheduler can interleave: LDS reads
   // run a few matrix products ahead of their use, and the rescale of O is
   // spread over the products of the preceding d subtile.
-  // Loads a matrix half-step issues for the next tiles (workgroup group 0):
-  // K rows kb_k.. into K buffer buf_k if k_on, V rows kb_v.. into V buffer
-  // buf_v if v_on.
+  // K loads a matrix half-step of group 0 issues for the next tile: key rows
+  // kb.. into K buffer buf, if on.
   struct Prefetch {
-    int kb_k, buf_k, kb_v, buf_v;
-    bool k_on, v_on;
+    int kb, buf;
+    bool on;
   };
   const i32x4 rsK = buffer_rsrc(kbase, (uint32_t)N * TL::kRowK);
-  const i32x4 rsV = buffer_rsrc(vbase, (uint32_t)N * TL::kRowV);
-  constexpr int NSEG = TL::kSegKPerWave + TL::kSegVPerWave;
-  // this wave's segment q of the request: K segments first, then V
+  constexpr int NSEG = TL::kSegKPerWave;
+  // this wave's K segment q of the request
   auto issue_one = [&](const int q, const Prefetch& rq) __attribute__((always_inline)) {
-    if (q < TL::kSegKPerWave) {
-      const int seg = wave + q * kWaves;
-      if (rq.k_on && (TL::kSegK % kWaves == 0 || seg < TL::kSegK))
-        lds_load16(rsK, voffK[q], (uint32_t)rq.kb_k * TL::kRowK,
-                   lds_address(smem) + rq.buf_k * TL::kBytesK + seg * 1024);
-    } else {
-      const int qv_ = q - TL::kSegKPerWave;
-      const int seg = wave + qv_ * kWaves;
-      if (rq.v_on && (TL::kSegV % kWaves == 0 || seg < TL::kSegV))
-        lds_load16(rsV, voffV[qv_], (uint32_t)rq.kb_v * TL::kRowV,
-                   lds_address(smem) + TL::kOffV + rq.buf_v * TL::kBytesV + seg * 1024);
-    }
+    const int seg = wg + q * TL::kIssuers;
+    if (rq.on && (TL::kSegK % TL::kIssuers == 0 || seg < TL::kSegK))
+      lds_load16(rsK, voff[q], (uint32_t)rq.kb * TL::kRowK,
+                 lds_address(smem) + rq.buf * TL::kBytesK + seg * 1024);
   };
 
   auto m_body = [&](const int j, auto do_pv_c, auto do_s_c, auto issue_c,
@@ -537,9 +534,7 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
         }
     } else {
       if constexpr (ISSUE) {
-        if (rq.k_on)
-          issue_k<D, QK, PV>(smem, wave, lane, rq.kb_k, rq.buf_k, kbase, sbase, N, voffK);
-        if (rq.v_on) issue_v<D, QK, PV>(smem, wave, rq.kb_v, rq.buf_v, vbase, N, voffV);
+        if (rq.on) issue_k<D, QK, PV>(smem, wg, lane, rq.kb, rq.buf, kbase, sbase, N, voff);
       }
       if constexpr (DO_PV) {
         const char* vt = (const char*)smem + TL::kOffV + ((j - 1) & 1) * TL::kBytesV;
@@ -653,16 +648,29 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
   // ================= X_j: online softmax of block j
   auto half_x = [&](const int j) __attribute__((always_inline)) {
     const int kb = j * BC;
-    // causal diagonal and ragged tail: invisible keys score -inf
+    // causal diagonal and ragged tail: invisible keys score -inf.  The test
+    // is per 32-key subtile first (uniform across the wave): subtiles wholly
+    // visible are left alone, wholly invisible ones are set to -inf, and
+    // only a subtile the diagonal or the sequence end crosses is masked
+    // element by element.
     const bool need_mask = (kb + BC > N) || (CAUSAL && kb + BC - 1 > q0w);
     if (need_mask) {
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks)
+      for (int ks = 0; ks < NKS; ++ks) {
+        const int k0s = kb + 32 * ks;
+        const bool all_vis = (k0s + 31 < N) && (!CAUSAL || k0s + 31 <= q0w);
+        const bool none_vis = (k0s >= N) || (CAUSAL && k0s > q0w + 31);
+        if (none_vis) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kb + 32 * ks + key_of_reg(r, g);
-          if (key >= N || (CAUSAL && key > qrow)) s[ks][r] = -INFINITY;
+          for (int r = 0; r < 16; ++r) s[ks][r] = -INFINITY;
+        } else if (!all_vis) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = k0s + key_of_reg(r, g);
+            if (key >= N || (CAUSAL && key > qrow)) s[ks][r] = -INFINITY;
+          }
         }
+      }
     }
     // bf16/fp32 Q,K: s holds raw dot products; the max is taken on them
     // (the scale is positive) and P = exp2(fma(s, c, -m)) with
@@ -720,22 +728,25 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
 
   // Group 0 runs slots (M_j, X_j) = (2j, 2j+1); group 1 runs (M_j, X_j) in
   // slots (2j+1, 2j+2) after an idle slot 0.  Both pass exactly 2*nblk + 2
-  // barriers, issue the loads of K_{j+1} and V_j at the start of slot 2j and
-  // await them at the end of slot 2j+1.  M_0 has no P.V part and M_nblk no
-  // S part; they are peeled off the loop, whose body is the full step.
+  // barriers.  Group 0 issues the loads of K_{j+1} during M_j (slot 2j),
+  // group 1 those of V_j at the start of slot 2j; each group awaits its own
+  // loads at the end of slot 2j+1, before slot 2j+2, the first that reads
+  // them.  The buffers they overwrite were last read in slot 2j-1.  M_0 has
+  // no P.V part and M_nblk no S part; they are peeled off the loop, whose
+  // body is the full step.
   constexpr BoolC<true> kYes{};
   constexpr BoolC<false> kNo{};
-  const Prefetch kNone{0, 0, 0, 0, false, false};
+  const Prefetch kNone{0, 0, false};
   if (group == 0) {
-    // slots 0, 1 (M_0 issues K_1 and V_0)
-    m_body(0, kNo, kYes, kYes, Prefetch{BC, 1, 0, 0, 1 < nblk, true});
+    // slots 0, 1
+    m_body(0, kNo, kYes, kYes, Prefetch{BC, 1, 1 < nblk});
     block_barrier();
     half_x(0);
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     block_barrier();
     for (int j = 1; j < nblk; ++j) {
-      // slots 2j, 2j+1 (M_j issues K_{j+1} and V_j)
-      m_body(j, kYes, kYes, kYes, Prefetch{(j + 1) * BC, (j + 1) & 1, j * BC, j & 1, j + 1 < nblk, true});
+      // slots 2j, 2j+1
+      m_body(j, kYes, kYes, kYes, Prefetch{(j + 1) * BC, (j + 1) & 1, j + 1 < nblk});
       block_barrier();
       half_x(j);
       __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
@@ -747,15 +758,13 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
     block_barrier();
   } else {
     // slot 0
-    if (1 < nblk) issue_k<D, QK, PV>(smem, wave, lane, BC, 1, kbase, sbase, N, voffK);
-    issue_v<D, QK, PV>(smem, wave, 0, 0, vbase, N, voffV);
+    issue_v<D, QK, PV>(smem, wg, 0, 0, vbase, N, voff);
     block_barrier();
     // slots 1, 2
     m_body(0, kNo, kYes, kNo, kNone);
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     block_barrier();
-    if (2 < nblk) issue_k<D, QK, PV>(smem, wave, lane, 2 * BC, 0, kbase, sbase, N, voffK);
-    if (1 < nblk) issue_v<D, QK, PV>(smem, wave, BC, 1, vbase, N, voffV);
+    if (1 < nblk) issue_v<D, QK, PV>(smem, wg, BC, 1, vbase, N, voff);
     half_x(0);
     block_barrier();
     for (int j = 1; j < nblk; ++j) {
@@ -763,9 +772,7 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
       m_body(j, kYes, kYes, kNo, kNone);
       __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
       block_barrier();
-      if (j + 2 < nblk)
-        issue_k<D, QK, PV>(smem, wave, lane, (j + 2) * BC, (j + 2) & 1, kbase, sbase, N, voffK);
-      if (j + 1 < nblk) issue_v<D, QK, PV>(smem, wave, (j + 1) * BC, (j + 1) & 1, vbase, N, voffV);
+      if (j + 1 < nblk) issue_v<D, QK, PV>(smem, wg, (j + 1) * BC, (j + 1) & 1, vbase, N, voff);
       half_x(j);
       block_barrier();
     }
