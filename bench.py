@@ -39,7 +39,7 @@ HBM_PEAK_GBS = 8000.0
 
 # HBM bytes per launch of the flash kernel on c3, from two rocprofv3 --pmc
 # passes (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch).  A plain 256 MiB
-# device copy reads FETCH_SIZE = 131084 KiB and WRITE_SIZE = 262144 KiB, so
+# device copy reads FETCH_SIZE = 131085 KiB and WRITE_SIZE = 262144 KiB, so
 # FETCH_SIZE is scaled by 2 and WRITE_SIZE by 1.  The figure is valid only for
 # the kernel sources it was taken on (sha256 of the files below).
 TRAFFIC_SOURCES = ("precision_numerics_amd/csrc/flash_fwd.hip",
@@ -47,9 +47,9 @@ TRAFFIC_SOURCES = ("precision_numerics_amd/csrc/flash_fwd.hip",
                    "precision_numerics_amd/csrc/launch.hpp")
 TRAFFIC = {
     "workload": "c3",
-    "sources_sha256": "5fa610c6448c4bfdabf97be49dad1c58114058d5d283eb700e9aee6dbf3cb2d1",
-    "fetch_kib": 690668.64, "fetch_scale": 2.0,
-    "write_kib": 131072.29, "write_scale": 1.0,
+    "sources_sha256": "7e8db7f29e88cec0cce02e70b880e70cd60942db7cdcc3e16aba54471de3356d",
+    "fetch_kib": 676981.0, "fetch_scale": 2.0,
+    "write_kib": 131072.0, "write_scale": 1.0,
 }
 
 
