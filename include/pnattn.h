@@ -69,8 +69,22 @@ typedef struct {
                         which then runs on bf16 MFMA; 0: keep P in fp32 and
                         run P*V on fp32 MFMA (V widened exactly)            */
   float softmax_scale; /* > 0; <= 0 selects 1/sqrt(head_dim)               */
-  int32_t stabilized;  /* reserved, must be 0                              */
-  float beta;          /* reserved, must be 0                              */
+  int32_t stabilized;  /* 0: FlashAttention as published.  1: the stabilised
+                          variant ("Why Low-Precision Transformer Training
+                          Fails", Figure 7 and Algorithm 1): when the running
+                          row maximum r_m of the scaled scores has occurred
+                          more than once, the normaliser of the
+                          probabilities becomes beta*r_m if r_m > 0 and 0 if
+                          r_m < 0 (r_m = 0 keeps 0), so that no unnormalised
+                          probability is exactly 1.  Occurrences are counted
+                          online over the key blocks processed so far.
+                          attn_fwd_flash with ATTN_BF16 only (ATTN_ERR_
+                          UNSUPPORTED otherwise; attn_fwd_baseline rejects
+                          it).  The output equals softmax(S)V in exact
+                          arithmetic either way; only rounding differs.     */
+  float beta;          /* stabilized = 1: the factor beta > 1 (finite); the
+                          page's own value is lost, so there is no default.
+                          stabilized = 0: must be 0.                        */
 } attn_problem_t;
 
 /* FlashAttention forward ("Why Low-Precision Transformer Training Fails",

@@ -133,11 +133,13 @@ def _contig(*ts):
 
 
 def make_problem(q, *, causal: bool, p_bf16: bool = True, softmax_scale: float = 0.0,
-                 dtype: Optional[int] = None) -> AttnProblem:
+                 dtype: Optional[int] = None, beta: Optional[float] = None) -> AttnProblem:
+    """beta (> 1) selects the stabilised flash variant; None the standard one."""
     b, h, n, d = q.shape
     return AttnProblem(b, h, n, d, int(bool(causal)),
                        _dtype_code(q) if dtype is None else dtype, int(bool(p_bf16)),
-                       float(softmax_scale), 0, 0.0)
+                       float(softmax_scale), 0 if beta is None else 1,
+                       0.0 if beta is None else float(beta))
 
 
 def _out_like(q, v):
@@ -148,11 +150,15 @@ def _out_like(q, v):
 
 
 def attn_fwd_flash(q, k, v, *, causal: bool, p_bf16: bool = True, softmax_scale: float = 0.0,
-                   q_scale=None, k_scale=None, out=None, lse=None, stream=None):
-    """FlashAttention forward; returns ``out`` ([B,H,N,d], dtype of v)."""
+                   q_scale=None, k_scale=None, out=None, lse=None, beta=None, stream=None):
+    """FlashAttention forward; returns ``out`` ([B,H,N,d], dtype of v).
+
+    beta (> 1, bf16 inputs only) runs the stabilised variant, whose
+    normaliser is beta*r_m (r_m > 0) or 0 (r_m < 0) when the row max r_m
+    occurs more than once."""
     _contig(q, k, v, q_scale, k_scale, out, lse)
     out = _out_like(q, v) if out is None else out
-    prob = make_problem(q, causal=causal, p_bf16=p_bf16, softmax_scale=softmax_scale)
+    prob = make_problem(q, causal=causal, p_bf16=p_bf16, softmax_scale=softmax_scale, beta=beta)
     _check(load().attn_fwd_flash(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(q_scale),
                                  _ptr(k_scale), _ptr(out), _ptr(lse), _stream(stream)))
     return out

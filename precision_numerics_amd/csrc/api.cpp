@@ -65,8 +65,17 @@ attn_status_t check_problem(const attn_problem_t* prob, const void* q, const voi
     return fail(ATTN_ERR_INVALID_ARG, "unknown dtype %d", prob->dtype);
   if (!std::isfinite(prob->softmax_scale))
     return fail(ATTN_ERR_INVALID_ARG, "softmax_scale is not finite");
-  if (prob->stabilized != 0 || prob->beta != 0.f)
-    return fail(ATTN_ERR_UNSUPPORTED, "stabilized/beta are reserved and must be 0");
+  if (prob->stabilized != 0 && prob->stabilized != 1)
+    return fail(ATTN_ERR_INVALID_ARG, "stabilized must be 0 or 1 (got %d)", prob->stabilized);
+  if (prob->stabilized == 0 && prob->beta != 0.f)
+    return fail(ATTN_ERR_INVALID_ARG, "beta must be 0 unless stabilized is 1");
+  if (prob->stabilized == 1) {
+    if (!(std::isfinite(prob->beta) && prob->beta > 1.f))
+      return fail(ATTN_ERR_INVALID_ARG, "stabilized needs a finite beta > 1 (got %g)",
+                  (double)prob->beta);
+    if (prob->dtype != ATTN_BF16)
+      return fail(ATTN_ERR_UNSUPPORTED, "the stabilized variant is built for ATTN_BF16 only");
+  }
   const bool i8 = prob->dtype == ATTN_INT8;
   if (i8 && (q_scale == nullptr || k_scale == nullptr))
     return fail(ATTN_ERR_INVALID_ARG, "ATTN_INT8 needs q_scale and k_scale");
@@ -88,6 +97,8 @@ attn_status_t check_problem(const attn_problem_t* prob, const void* q, const voi
   a->causal = prob->causal;
   a->dtype = prob->dtype;
   a->p_bf16 = prob->p_bf16;
+  a->stabilized = prob->stabilized;
+  a->beta = prob->beta;
   a->scale = prob->softmax_scale > 0.f
                  ? prob->softmax_scale
                  : (float)(1.0 / std::sqrt((double)prob->head_dim));
@@ -160,6 +171,8 @@ attn_status_t attn_fwd_baseline(const attn_problem_t* prob, const void* q, const
   bool empty = false;
   attn_status_t st = check_problem(prob, q, k, v, q_scale, k_scale, o, &a, &empty);
   if (st != ATTN_OK) return st;
+  if (prob->stabilized != 0)
+    return fail(ATTN_ERR_UNSUPPORTED, "the stabilized variant is a flash-kernel option");
   if (empty) return ok();
   const int64_t bh = prob->batch * prob->heads;
   if (bh > kMaxGridYZ)

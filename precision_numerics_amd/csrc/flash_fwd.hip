@@ -112,6 +112,7 @@ struct FlashParams {
   int n;             // sequence length
   float scale_log2;  // softmax scale * log2(e)
   int p_round;       // fp32 P*V engines: round P to bf16 values first
+  float beta;        // stabilised variant: normaliser factor for a repeated positive max
 };
 
 // Key (0..31 inside a 32-key subtile) that row m of the K operand carries.
@@ -330,7 +331,7 @@ __device__ __forceinline__ void block_barrier() {
 // are awaited at the end of slot 2j+1, so they land before slot 2j+2, the
 // first slot that reads them.  The buffers they overwrite were last read in
 // slot 2j-1.
-template <int D, int QK, int PV, bool CAUSAL, bool DEBUG_S>
+template <int D, int QK, int PV, bool CAUSAL, bool DEBUG_S, bool STAB>
 __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
   using QT = typename QKTraits<QK>::T;
   using VT = typename VTraits<PV>::T;
@@ -408,9 +409,10 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
   // nothing to O.  Running it keeps the loop free of per-wave conditions,
   // whose merging paths would keep dead score registers alive.
 
-  float m_run = -INFINITY;     // running max in log2 units
+  float m_run = -INFINITY;     // normaliser of the accumulated block sums, log2 units
   float mraw_run = -INFINITY;  // running max of the unscaled scores
   float l_run = 0.f;
+  int nmax_run = 0;            // stabilised variant: occurrences of the running max
   f32x16 oacc[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x16{};
@@ -682,11 +684,32 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
     float mx = tree_max(flat);
     mx = pair32_max(mx);
     const float mraw_new = fmaxf(mraw_run, mx);
+    // normaliser m of this block's probabilities P = exp2(s*c - m), in log2
+    // units (int8: s is already scaled)
+    float m_use = (QK == QK_I8) ? mraw_new : mraw_new * p.scale_log2;
+    if constexpr (STAB) {
+      // Stabilised variant ("Why Low-Precision Transformer Training Fails",
+      // Figure 7 and Algorithm 1): when the row maximum r_m occurs more than
+      // once, the normaliser becomes beta*r_m (r_m > 0) or 0 (r_m < 0), so
+      // that no probability is exactly 1.  Occurrences are counted online:
+      // those of this block's max in this block, added to the running count
+      // while the running max is unchanged.
+      int cnt = 0;
+      if (mx != -INFINITY) {
+#pragma unroll
+        for (int i = 0; i < NKS * 16; ++i) cnt += (flat[i] == mx) ? 1 : 0;
+      }
+      cnt = pair32_isum(cnt);
+      nmax_run = (mx > mraw_run) ? cnt : (mx == mraw_run ? nmax_run + cnt : nmax_run);
+      if (nmax_run >= 2) {
+        if (mraw_new > 0.f) m_use *= p.beta;
+        else if (mraw_new < 0.f) m_use = 0.f;
+      }
+    }
     mraw_run = mraw_new;
-    const float m_new = (QK == QK_I8) ? mraw_new : mraw_new * p.scale_log2;
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    if (m_use == -INFINITY) m_use = 0.f;  // every score so far masked
     const float alpha = exp2_approx(m_run - m_use);
-    m_run = m_new;
+    m_run = (mraw_new == -INFINITY) ? -INFINITY : m_use;
     // four independent partial row sums (a single += chain would serialise
     // on the add latency)
     float rsum[4] = {0.f, 0.f, 0.f, 0.f};
@@ -724,6 +747,7 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
     pin(l_run);
     pin(m_run);
     pin(mraw_run);
+    if constexpr (STAB) pin(nmax_run);
   };
 
   // Group 0 runs slots (M_j, X_j) = (2j, 2j+1); group 1 runs (M_j, X_j) in
@@ -807,18 +831,18 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
   }
 }
 
-template <int D, int QK, int PV, bool CAUSAL, bool DEBUG_S>
+template <int D, int QK, int PV, bool CAUSAL, bool DEBUG_S, bool STAB>
 hipError_t launch_t(const FlashParams& fp, int64_t bh, int ntiles, hipStream_t st) {
   dim3 grid((unsigned)bh, (unsigned)ntiles, 1);
-  hipLaunchKernelGGL((flash_fwd_kernel<D, QK, PV, CAUSAL, DEBUG_S>), grid, dim3(kThreads), 0,
-                     st, fp);
+  hipLaunchKernelGGL((flash_fwd_kernel<D, QK, PV, CAUSAL, DEBUG_S, STAB>), grid,
+                     dim3(kThreads), 0, st, fp);
   return hipGetLastError();
 }
 
-template <int D, int QK, int PV, bool DEBUG_S>
+template <int D, int QK, int PV, bool DEBUG_S, bool STAB = false>
 hipError_t launch_c(const FlashParams& fp, bool causal, int64_t bh, int nt, hipStream_t st) {
-  return causal ? launch_t<D, QK, PV, true, DEBUG_S>(fp, bh, nt, st)
-                : launch_t<D, QK, PV, false, DEBUG_S>(fp, bh, nt, st);
+  return causal ? launch_t<D, QK, PV, true, DEBUG_S, STAB>(fp, bh, nt, st)
+                : launch_t<D, QK, PV, false, DEBUG_S, STAB>(fp, bh, nt, st);
 }
 
 template <int D>
@@ -829,6 +853,9 @@ hipError_t launch_d(const AttnArgs& a, const FlashParams& fp, int64_t bh, int nt
     case kF32:
       return launch_c<D, QK_F32, PV_F32_VF32, false>(fp, c, bh, nt, st);
     case kBF16:
+      if (a.stabilized)
+        return a.p_bf16 ? launch_c<D, QK_BF16, PV_BF16, false, true>(fp, c, bh, nt, st)
+                        : launch_c<D, QK_BF16, PV_F32_VBF16, false, true>(fp, c, bh, nt, st);
       return a.p_bf16 ? launch_c<D, QK_BF16, PV_BF16, false>(fp, c, bh, nt, st)
                       : launch_c<D, QK_BF16, PV_F32_VBF16, false>(fp, c, bh, nt, st);
     case kINT8:
@@ -856,6 +883,7 @@ hipError_t launch_flash(const AttnArgs& a, hipStream_t stream) {
   fp.n = (int)a.seq_len;
   fp.scale_log2 = (float)((double)a.scale * 1.4426950408889634);
   fp.p_round = (a.dtype == kF32) ? a.p_bf16 : 0;
+  fp.beta = a.beta;
   const int64_t bh = a.batch * a.heads;
   const int ntiles = (int)((a.seq_len + kBR - 1) / kBR);
   if (a.head_dim == 64) return launch_d<64>(a, fp, bh, ntiles, stream);

@@ -24,6 +24,8 @@ struct AttnArgs {
   int dtype = kBF16;
   int p_bf16 = 1;
   float scale = 0.f;  // resolved softmax scale (> 0)
+  int stabilized = 0; // flash only: the repeated-max normaliser variant
+  float beta = 0.f;   // its factor (> 1) for a repeated positive max
 };
 
 // Flash forward; returns the launch status.

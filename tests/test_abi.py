@@ -57,7 +57,12 @@ FAKE = 0x1000  # never dereferenced: every case below fails validation first
     (dict(p_bf16=7), B.ATTN_ERR_INVALID_ARG),
     (dict(dtype=9), B.ATTN_ERR_INVALID_ARG),
     (dict(softmax_scale=float("nan")), B.ATTN_ERR_INVALID_ARG),
-    (dict(stabilized=1), B.ATTN_ERR_UNSUPPORTED),
+    (dict(stabilized=1), B.ATTN_ERR_INVALID_ARG),            # beta missing
+    (dict(stabilized=1, beta=1.0), B.ATTN_ERR_INVALID_ARG),  # beta must exceed 1
+    (dict(stabilized=1, beta=float("inf")), B.ATTN_ERR_INVALID_ARG),
+    (dict(stabilized=2, beta=2.0), B.ATTN_ERR_INVALID_ARG),
+    (dict(stabilized=0, beta=2.0), B.ATTN_ERR_INVALID_ARG),  # beta without the variant
+    (dict(stabilized=1, beta=2.0, dtype=B.ATTN_F32), B.ATTN_ERR_UNSUPPORTED),
     (dict(dtype=B.ATTN_INT8), B.ATTN_ERR_INVALID_ARG),       # scales missing
 ])
 def test_flash_validation(clib, kw, status):
@@ -65,6 +70,14 @@ def test_flash_validation(clib, kw, status):
     rc = clib.attn_fwd_flash(ctypes.byref(p), FAKE, FAKE, FAKE, None, None, FAKE, None, None)
     assert rc == status
     assert clib.attn_last_error().decode()
+
+
+def test_baseline_rejects_stabilized(clib):
+    p = _prob(stabilized=1, beta=2.0)
+    rc = clib.attn_fwd_baseline(ctypes.byref(p), FAKE, FAKE, FAKE, None, None, FAKE, 1 << 20,
+                                FAKE, None)
+    assert rc == B.ATTN_ERR_UNSUPPORTED
+    assert "flash" in clib.attn_last_error().decode()
 
 
 def test_null_pointers_rejected(clib):
