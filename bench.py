@@ -139,6 +139,55 @@ def cpu_baseline(cfg, inp, units, workers):
     return np.stack(outs), stats
 
 
+def bias_leg(pna, torch, workers, beta=2.0, units=(0, 31), v_shift=-2.0):
+    """Rounding bias of standard versus stabilised FlashAttention on the
+    rank-4 long-sequence workload: signed and absolute error against the FP64
+    oracle on sampled heads, for P rounded to bf16 and P kept in fp32.
+    Variants: V as drawn; V shifted to a negative mean (most columns of V
+    negative, the situation the low-precision training page's Figure 5
+    examines); and that with the key rows duplicated in pairs (every token
+    appears twice), so that each row maximum is repeated."""
+    import oracle
+    cfg = synth.CONFIGS["c4"]
+    b, h, n, d = cfg.shape
+    inp = synth.make_inputs(cfg)
+    q, k, v = to_device(inp)
+    v_neg_bits = synth.f32_to_bf16_bits(synth.bf16_bits_to_f32(inp.v) + np.float32(v_shift))
+    k_pair_bits = inp.k.reshape(b, h, n // 2, 2, d)[:, :, :, :1, :].repeat(2, axis=3)
+    k_pair_bits = np.ascontiguousarray(k_pair_bits.reshape(b, h, n, d))
+
+    def dev_bf16(bits):
+        return torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
+    qf = synth.bf16_bits_to_f32(inp.q).reshape(b * h, n, d)
+    scale = oracle.default_scale(d)
+    out = {"workload": f"c4: {cfg.description}", "beta": beta, "units": list(units),
+           "v_shift": v_shift}
+    variants = (("v", k, inp.k, v, inp.v),
+                ("v_shifted", k, inp.k, dev_bf16(v_neg_bits), v_neg_bits),
+                ("v_shifted_keys_paired", dev_bf16(k_pair_bits), k_pair_bits,
+                 dev_bf16(v_neg_bits), v_neg_bits))
+    for vname, kt, kbits, vt, vbits in variants:
+        kf = synth.bf16_bits_to_f32(kbits).reshape(b * h, n, d)
+        vf = synth.bf16_bits_to_f32(vbits).reshape(b * h, n, d)
+
+        def unit(u, kf=kf, vf=vf):
+            return oracle.attention_head(qf[u], kf[u], vf[u], causal=True, scale=scale)[0]
+        refs, _ = oracle.run_heads(unit, list(units), workers=workers)
+        ref_t = torch.from_numpy(np.stack(refs)).cuda()
+        res = {}
+        for p_bf16 in (True, False):
+            row = {}
+            for kind, bb in (("standard", None), ("stabilized", beta)):
+                o = pna.attn_fwd_flash(q, kt, vt, causal=True, p_bf16=p_bf16, beta=bb)
+                o_s = torch.stack([o.view(b * h, n, d)[u] for u in units]).contiguous()
+                dev = pna.attn_deviation(o_s, ref_t)
+                row[kind] = {key: dev[key] for key in ("mean_signed", "mean_abs", "max_abs",
+                                                       "rms")}
+            res["p_bf16" if p_bf16 else "p_fp32"] = row
+        out[vname] = res
+    return out
+
+
 def copy_probe():
     """A plain device copy of known size, for scaling the FETCH_SIZE and
     WRITE_SIZE counters (read 256 MiB, write 256 MiB per launch)."""
@@ -300,6 +349,12 @@ def main():
                                      "note": "includes the host synchronisation per call"}
             except Exception as exc:                     # noqa: BLE001
                 legs["deviation"] = {"error": repr(exc)}
+        try:
+            log("bench: rounding-bias leg (c4, standard vs stabilised)")
+            workers = min(args.cpu_workers, len(os.sched_getaffinity(0)))
+            legs["rounding_bias"] = bias_leg(pna, torch, workers)
+        except Exception as exc:                         # noqa: BLE001
+            legs["rounding_bias"] = {"error": repr(exc)}
         try:
             log("bench: int8 quantiser leg")
             x = torch.randn(cfg.batch * cfg.heads * cfg.seq_len, cfg.head_dim, device="cuda")
