@@ -6,8 +6,9 @@ never do, and this package never imports them.
 """
 from .attention import (default_scale, attention, attention_head, int8_scores,
                         attention_int8, attention_int8_head, quantize_int8,
-                        deviation, attention_probabilities, run_heads)
+                        deviation, attention_probabilities, attention_delta,
+                        run_heads)
 
 __all__ = ["default_scale", "attention", "attention_head", "int8_scores",
            "attention_int8", "attention_int8_head", "quantize_int8",
-           "deviation", "attention_probabilities", "run_heads"]
+           "deviation", "attention_probabilities", "attention_delta", "run_heads"]

@@ -25,6 +25,10 @@ What it computes, and the passages it follows
   of the same isolated forward pass ("Is Flash Attention Stable?", abstract;
   O_lp versus O_hp in "Why Low-Precision Transformer Training Fails",
   Figures 5 and 6) is summarised by :func:`deviation`.
+* The quantity the backward pass derives from the forward output,
+  delta = rowsum(dO * O) ("Why Low-Precision Transformer Training Fails",
+  Figure 5 caption and the section that isolates the error in O: delta_lp
+  computed from the low-precision O), is :func:`attention_delta`.
 * INT8 attention compatible with the FlashAttention forward workflow
   ("INT-FlashAttention", abstract): the scores are the exact integer dot
   products of int8 codes times the per-row scales.  The pages do not give the
@@ -46,7 +50,7 @@ import numpy as np
 __all__ = [
     "default_scale", "attention", "attention_head", "int8_scores",
     "attention_int8", "attention_int8_head", "quantize_int8", "deviation",
-    "attention_probabilities", "run_heads",
+    "attention_probabilities", "attention_delta", "run_heads",
 ]
 
 
@@ -209,6 +213,21 @@ def attention_int8(q_codes, q_scale, k_codes, k_scale, v, *, causal: bool,
                                            causal=causal, scale=scale,
                                            block_rows=block_rows)
     return o.reshape(vv.shape), lse.reshape(lead + (n,))
+
+
+# ---------------------------------------------------------------------------
+# delta = rowsum(dO * O), the backward pass's per-row term
+# ---------------------------------------------------------------------------
+
+def attention_delta(o, d_o) -> np.ndarray:
+    """delta_i = sum_c dO[i, c] * O[i, c] over the last axis, in float64
+    ("Why Low-Precision Transformer Training Fails": delta = rowsum(dO o O),
+    Figure 5 caption).  o and d_o: [..., N, d] of the same shape."""
+    o64 = np.asarray(o, dtype=np.float64)
+    g64 = np.asarray(d_o, dtype=np.float64)
+    assert o64.shape == g64.shape
+    prod = g64 * o64
+    return prod.sum(axis=-1)
 
 
 # ---------------------------------------------------------------------------

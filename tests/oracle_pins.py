@@ -338,3 +338,39 @@ def check_deviation(ora):
     assert st["argmax"] == 10 and st["max_abs"] == 1.0 and st["n_nonfinite"] == 2
     assert st["mean_abs"] == 2.0 / 998
     assert ora.deviation(ref, ref)["max_abs"] == 0.0
+
+
+# ---------------------------------------------------------------------------
+# delta = rowsum(dO * O)
+# ---------------------------------------------------------------------------
+
+@pin
+def check_delta(ora):
+    """Brute force with exact float sums; closed forms (dO = O gives the row's
+    squared norm, a unit dO picks one column); and the backward identity
+    rowsum(dO o O) = rowsum(P o (dO V^T)) for O = P V, which ties delta to
+    the attention probabilities."""
+    rng = _rng(41)
+    o = rng.standard_normal((3, 5, 7))
+    g = rng.standard_normal((3, 5, 7))
+    got = ora.attention_delta(o, g)
+    assert got.shape == (3, 5)
+    for a in range(3):
+        for i in range(5):
+            exact = math.fsum(float(g[a, i, c]) * float(o[a, i, c]) for c in range(7))
+            assert abs(got[a, i] - exact) <= 1e-14 * max(1.0, abs(exact))
+    sq = ora.attention_delta(o, o)
+    assert np.allclose(sq, (o ** 2).sum(-1), rtol=1e-14, atol=0)
+    e2 = np.zeros_like(o)
+    e2[..., 2] = 1.0
+    assert np.array_equal(ora.attention_delta(o, e2), o[..., 2])
+    # delta through the attention probabilities
+    q = rng.standard_normal((9, 4))
+    k = rng.standard_normal((9, 4))
+    v = rng.standard_normal((9, 6))
+    d_o = rng.standard_normal((9, 6))
+    for causal in (False, True):
+        out, _ = ora.attention(q, k, v, causal=causal, scale=0.5)
+        p = ora.attention_probabilities(q, k, causal=causal, scale=0.5)
+        via_p = (p * (d_o @ v.T)).sum(axis=1)
+        assert np.allclose(ora.attention_delta(out, d_o), via_p, rtol=1e-12, atol=1e-13)

@@ -63,6 +63,11 @@ MUTANTS = [
      "mean_abs=float(np.abs(ef).sum() / n)"),
     ("rms without root", "rms=float(math.sqrt((ef * ef).sum() / n_fin))",
      "rms=float((ef * ef).sum() / n_fin)"),
+    ("delta sums over rows", "return prod.sum(axis=-1)", "return prod.sum(axis=-2)"),
+    ("delta drops the last column", "return prod.sum(axis=-1)",
+     "return prod[..., :-1].sum(axis=-1)"),
+    ("delta adds instead of multiplying", "prod = g64 * o64", "prod = g64 + o64"),
+    ("delta squares O", "prod = g64 * o64", "prod = o64 * o64"),
 ]
 
 
