@@ -139,52 +139,73 @@ def cpu_baseline(cfg, inp, units, workers):
     return np.stack(outs), stats
 
 
-def bias_leg(pna, torch, workers, beta=2.0, units=(0, 31), v_shift=-2.0):
-    """Rounding bias of standard versus stabilised FlashAttention on the
-    rank-4 long-sequence workload: signed and absolute error against the FP64
-    oracle on sampled heads, for P rounded to bf16 and P kept in fp32.
-    Variants: V as drawn; V shifted to a negative mean (most columns of V
-    negative, the situation the low-precision training page's Figure 5
-    examines); and that with the key rows duplicated in pairs (every token
-    appears twice), so that each row maximum is repeated."""
-    import oracle
+BIAS_BETA = 2.0
+BIAS_UNITS = (0, 31)
+BIAS_V_SHIFT = -2.0
+
+
+def bias_inputs():
+    """Inputs of the rounding-bias leg: the rank-4 long-sequence workload with
+    V as drawn, V shifted to a negative mean (most columns of V negative, the
+    situation the low-precision training page's Figure 5 examines), and that
+    with the key rows duplicated in pairs (every token appears twice, so each
+    row maximum is repeated).  Returns (cfg, q bits, [(name, k bits, v bits)])."""
     cfg = synth.CONFIGS["c4"]
     b, h, n, d = cfg.shape
     inp = synth.make_inputs(cfg)
-    q, k, v = to_device(inp)
-    v_neg_bits = synth.f32_to_bf16_bits(synth.bf16_bits_to_f32(inp.v) + np.float32(v_shift))
-    k_pair_bits = inp.k.reshape(b, h, n // 2, 2, d)[:, :, :, :1, :].repeat(2, axis=3)
-    k_pair_bits = np.ascontiguousarray(k_pair_bits.reshape(b, h, n, d))
+    v_neg = synth.f32_to_bf16_bits(synth.bf16_bits_to_f32(inp.v) + np.float32(BIAS_V_SHIFT))
+    k_pair = inp.k.reshape(b, h, n // 2, 2, d)[:, :, :, :1, :].repeat(2, axis=3)
+    k_pair = np.ascontiguousarray(k_pair.reshape(b, h, n, d))
+    return cfg, inp.q, [("v", inp.k, inp.v), ("v_shifted", inp.k, v_neg),
+                        ("v_shifted_keys_paired", k_pair, v_neg)]
 
-    def dev_bf16(bits):
-        return torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
-    qf = synth.bf16_bits_to_f32(inp.q).reshape(b * h, n, d)
+
+def cpu_baseline_bias_refs(workers):
+    """Part of the CPU-baseline leg: the FP64 oracle outputs of the sampled
+    heads of every rounding-bias variant."""
+    import oracle
+    cfg, qbits, variants = bias_inputs()
+    b, h, n, d = cfg.shape
+    qf = synth.bf16_bits_to_f32(qbits).reshape(b * h, n, d)
     scale = oracle.default_scale(d)
-    out = {"workload": f"c4: {cfg.description}", "beta": beta, "units": list(units),
-           "v_shift": v_shift}
-    variants = (("v", k, inp.k, v, inp.v),
-                ("v_shifted", k, inp.k, dev_bf16(v_neg_bits), v_neg_bits),
-                ("v_shifted_keys_paired", dev_bf16(k_pair_bits), k_pair_bits,
-                 dev_bf16(v_neg_bits), v_neg_bits))
-    for vname, kt, kbits, vt, vbits in variants:
+    refs = {}
+    for name, kbits, vbits in variants:
         kf = synth.bf16_bits_to_f32(kbits).reshape(b * h, n, d)
         vf = synth.bf16_bits_to_f32(vbits).reshape(b * h, n, d)
 
         def unit(u, kf=kf, vf=vf):
             return oracle.attention_head(qf[u], kf[u], vf[u], causal=True, scale=scale)[0]
-        refs, _ = oracle.run_heads(unit, list(units), workers=workers)
-        ref_t = torch.from_numpy(np.stack(refs)).cuda()
+        outs, _ = oracle.run_heads(unit, list(BIAS_UNITS), workers=workers)
+        refs[name] = np.stack(outs)
+    return refs
+
+
+def bias_leg(pna, torch, refs):
+    """Rounding bias of standard versus stabilised FlashAttention: signed and
+    absolute error against the FP64 references of the sampled heads, for P
+    rounded to bf16 and P kept in fp32."""
+    cfg, qbits, variants = bias_inputs()
+    b, h, n, d = cfg.shape
+
+    def dev_bf16(bits):
+        return torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
+    q = dev_bf16(qbits)
+    out = {"workload": f"c4: {cfg.description}", "beta": BIAS_BETA, "units": list(BIAS_UNITS),
+           "v_shift": BIAS_V_SHIFT}
+    for name, kbits, vbits in variants:
+        kt, vt = dev_bf16(kbits), dev_bf16(vbits)
+        ref_t = torch.from_numpy(refs[name]).cuda()
         res = {}
         for p_bf16 in (True, False):
             row = {}
-            for kind, bb in (("standard", None), ("stabilized", beta)):
+            for kind, bb in (("standard", None), ("stabilized", BIAS_BETA)):
                 o = pna.attn_fwd_flash(q, kt, vt, causal=True, p_bf16=p_bf16, beta=bb)
-                o_s = torch.stack([o.view(b * h, n, d)[u] for u in units]).contiguous()
+                o_s = torch.stack([o.view(b * h, n, d)[u] for u in BIAS_UNITS]).contiguous()
                 dev = pna.attn_deviation(o_s, ref_t)
                 row[kind] = {key: dev[key] for key in ("mean_signed", "mean_abs", "max_abs",
                                                        "rms")}
             res["p_bf16" if p_bf16 else "p_fp32"] = row
-        out[vname] = res
+        out[name] = res
     return out
 
 
@@ -303,9 +324,14 @@ def main():
         result["cpu_baseline"]["seconds"] = round(cpu["seconds"], 3)
         result["gpu_over_cpu"] = round(tflops / cpu["value"], 1)
         ref_t = torch.from_numpy(ref).cuda()
+        bias_refs = None
+        if not args.no_legs:
+            log("bench: FP64 oracle references for the rounding-bias leg")
+            bias_refs = cpu_baseline_bias_refs(workers)
     else:
         result["cpu_baseline"] = None
         ref_t = None
+        bias_refs = None
 
     # ---- other kernels of the path, each timed alone
     if not args.no_legs:
@@ -349,12 +375,23 @@ def main():
                                      "note": "includes the host synchronisation per call"}
             except Exception as exc:                     # noqa: BLE001
                 legs["deviation"] = {"error": repr(exc)}
+        if bias_refs is not None:
+            try:
+                log("bench: rounding-bias leg (c4, standard vs stabilised)")
+                legs["rounding_bias"] = bias_leg(pna, torch, bias_refs)
+            except Exception as exc:                     # noqa: BLE001
+                legs["rounding_bias"] = {"error": repr(exc)}
         try:
-            log("bench: rounding-bias leg (c4, standard vs stabilised)")
-            workers = min(args.cpu_workers, len(os.sched_getaffinity(0)))
-            legs["rounding_bias"] = bias_leg(pna, torch, workers)
+            log("bench: delta = rowsum(dO * O) leg")
+            g = torch.randn(out.shape, device="cuda").to(out.dtype)
+            dl = torch.empty(out.shape[:-1], dtype=torch.float32, device="cuda")
+            dms = event_time_ms(lambda: pna.attn_bwd_delta(out, g, delta=dl), 20, 3)
+            nb = 2 * out.numel() * out.element_size() + dl.numel() * 4
+            legs["bwd_delta"] = {"ms": round(dms, 4), "alg_bytes": nb,
+                                 "GB_per_s": round(nb / (dms * 1e-3) / 1e9, 1),
+                                 "hbm_frac": round(nb / (dms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
         except Exception as exc:                         # noqa: BLE001
-            legs["rounding_bias"] = {"error": repr(exc)}
+            legs["bwd_delta"] = {"error": repr(exc)}
         try:
             log("bench: int8 quantiser leg")
             x = torch.randn(cfg.batch * cfg.heads * cfg.seq_len, cfg.head_dim, device="cuda")

@@ -158,6 +158,22 @@ attn_status_t attn_deviation(const void* o_test, int32_t o_dtype,
                              size_t scratch_bytes, attn_deviation_t* out_host,
                              void* stream);
 
+/* delta = rowsum(dO o O): for every row i of every (batch, head),
+ * delta_i = sum_c dO[i,c] * O[i,c] -- the per-row term the attention backward
+ * pass derives from the forward output ("Why Low-Precision Transformer
+ * Training Fails", Figure 5 caption; that page traces the training failure
+ * to delta computed from the low-precision O).
+ *   prob  : sizes and dtype as for the forward call (causal, p_bf16,
+ *           softmax_scale, stabilized and beta are not used)
+ *   o, d_o: [B,H,N,d] in the forward output dtype (fp32 for ATTN_F32,
+ *           bf16 otherwise)
+ *   delta : [B,H,N] fp32
+ * One fused multiply-add per element in fp32 (bf16 products are exact),
+ * then a fixed-order combination of the partial sums: bitwise
+ * reproducible.  A zero size validates and returns ATTN_OK.              */
+attn_status_t attn_bwd_delta(const attn_problem_t* prob, const void* o,
+                             const void* d_o, float* delta, void* stream);
+
 /* Symmetric per-row int8 quantisation of fp32 rows x [rows][d] (the int8
  * Q/K input of "INT-FlashAttention", abstract; the per-row absmax/127
  * granularity is this library's reading):

@@ -69,6 +69,7 @@ _SIGNATURES = {
     "attn_deviation": [_P, ctypes.c_int32, _P, ctypes.c_int64, _P, ctypes.c_size_t,
                        ctypes.POINTER(AttnDeviation), _P],
     "attn_quantize_int8": [_P, ctypes.c_int64, ctypes.c_int64, _P, _P, _P],
+    "attn_bwd_delta": [ctypes.POINTER(AttnProblem), _P, _P, _P, _P],
     "attn_status_string": [ctypes.c_int],
     "attn_last_error": [],
     "attn_version": [],
@@ -239,6 +240,22 @@ def attn_quantize_int8(x, *, codes=None, scales=None, stream=None):
     _check(load().attn_quantize_int8(_ptr(x), rows, d, _ptr(codes), _ptr(scales),
                                      _stream(stream)))
     return codes, scales
+
+
+def attn_bwd_delta(o, d_o, *, delta=None, stream=None):
+    """delta = rowsum(d_o * o) over the last axis ([B,H,N,d] -> [B,H,N] fp32)."""
+    import torch
+    _contig(o, d_o, delta)
+    if o.shape != d_o.shape or o.dtype != d_o.dtype:
+        raise ValueError("o and d_o must have the same shape and dtype")
+    b, h, n, d = o.shape
+    delta = (torch.empty((b, h, n), dtype=torch.float32, device=o.device)
+             if delta is None else delta)
+    code = ATTN_F32 if o.dtype == torch.float32 else ATTN_BF16
+    prob = AttnProblem(b, h, n, d, 0, code, 1, 0.0, 0, 0.0)
+    _check(load().attn_bwd_delta(ctypes.byref(prob), _ptr(o), _ptr(d_o), _ptr(delta),
+                                 _stream(stream)))
+    return delta
 
 
 def attn_version() -> str:

@@ -122,7 +122,35 @@ const char* attn_status_string(attn_status_t s) {
 
 const char* attn_last_error(void) { return g_last_error.c_str(); }
 
-const char* attn_version(void) { return "pnattn 0.1.0 (gfx950)"; }
+const char* attn_version(void) { return "pnattn 0.2.0 (gfx950)"; }
+
+attn_status_t attn_bwd_delta(const attn_problem_t* prob, const void* o, const void* d_o,
+                             float* delta, void* stream) {
+  if (prob == nullptr) return fail(ATTN_ERR_INVALID_ARG, "prob is NULL");
+  if (prob->batch < 0 || prob->heads < 0 || prob->seq_len < 0)
+    return fail(ATTN_ERR_INVALID_ARG, "negative size");
+  if (prob->head_dim <= 0)
+    return fail(ATTN_ERR_INVALID_ARG, "head_dim must be positive (got %lld)",
+                (long long)prob->head_dim);
+  if (prob->head_dim != 64 && prob->head_dim != 128)
+    return fail(ATTN_ERR_UNSUPPORTED, "head_dim %lld not built (64 or 128)",
+                (long long)prob->head_dim);
+  if (prob->dtype != ATTN_F32 && prob->dtype != ATTN_BF16 && prob->dtype != ATTN_INT8)
+    return fail(ATTN_ERR_INVALID_ARG, "unknown dtype %d", prob->dtype);
+  if (prob->batch > 0 && prob->heads > INT64_MAX / prob->batch)
+    return fail(ATTN_ERR_UNSUPPORTED, "batch*heads too large");
+  const int64_t bh = prob->batch * prob->heads;
+  if (bh > 0 && prob->seq_len > INT64_MAX / 128 / bh)
+    return fail(ATTN_ERR_UNSUPPORTED, "problem too large");
+  const int64_t rows = bh * prob->seq_len;
+  if (rows == 0) return ok();
+  if (o == nullptr || d_o == nullptr || delta == nullptr)
+    return fail(ATTN_ERR_INVALID_ARG, "o, d_o and delta must be non-NULL");
+  const int out = prob->dtype == ATTN_F32 ? pn::kF32 : pn::kBF16;
+  return from_hip(pn::launch_delta(o, d_o, out, (int)prob->head_dim, rows, delta,
+                                   (hipStream_t)stream),
+                  "attn_bwd_delta launch");
+}
 
 attn_status_t attn_fwd_flash(const attn_problem_t* prob, const void* q, const void* k,
                              const void* v, const float* q_scale, const float* k_scale,

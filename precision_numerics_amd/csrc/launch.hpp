@@ -46,6 +46,11 @@ hipError_t launch_deviation(const void* o_test, int o_dtype,
                             const double* o_ref, int64_t n, void* scratch,
                             DeviationRecord* out_host, hipStream_t stream);
 
+// delta = rowsum(dO o O) over rows of head_dim elements of the output dtype
+// (kF32, or bf16 for the others).
+hipError_t launch_delta(const void* o, const void* d_o, int out_dtype, int head_dim,
+                        int64_t rows, float* delta, hipStream_t stream);
+
 hipError_t launch_quantize(const float* x, int64_t rows, int64_t d,
                            int8_t* codes, float* scales, hipStream_t stream);
 

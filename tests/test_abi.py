@@ -80,6 +80,19 @@ def test_baseline_rejects_stabilized(clib):
     assert "flash" in clib.attn_last_error().decode()
 
 
+def test_delta_validation(clib):
+    p = _prob()
+    assert clib.attn_bwd_delta(None, FAKE, FAKE, FAKE, None) == B.ATTN_ERR_INVALID_ARG
+    assert clib.attn_bwd_delta(ctypes.byref(p), None, FAKE, FAKE, None) == B.ATTN_ERR_INVALID_ARG
+    assert clib.attn_bwd_delta(ctypes.byref(p), FAKE, FAKE, None, None) == B.ATTN_ERR_INVALID_ARG
+    bad = _prob(head_dim=80)
+    assert clib.attn_bwd_delta(ctypes.byref(bad), FAKE, FAKE, FAKE, None) == B.ATTN_ERR_UNSUPPORTED
+    bad = _prob(dtype=5)
+    assert clib.attn_bwd_delta(ctypes.byref(bad), FAKE, FAKE, FAKE, None) == B.ATTN_ERR_INVALID_ARG
+    empty = _prob(seq_len=0)
+    assert clib.attn_bwd_delta(ctypes.byref(empty), None, None, None, None) == B.ATTN_OK
+
+
 def test_null_pointers_rejected(clib):
     p = _prob()
     assert clib.attn_fwd_flash(None, FAKE, FAKE, FAKE, None, None, FAKE, None, None) == 1
