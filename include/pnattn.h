@@ -58,9 +58,10 @@ typedef struct {
   int64_t batch;     /* >= 0 (0, like any zero size, is an empty problem:
                         the call validates and returns ATTN_OK, launching
                         nothing)                                            */
-  int64_t heads;     /* >= 0                                               */
+  int64_t heads;     /* >= 0; batch*heads < 2^31                           */
   int64_t seq_len;   /* N >= 0, at most 2^22; queries and keys have the
-                        same length                                         */
+                        same length; batch*heads*ceil(N/256) at most 2^30
+                        (ATTN_ERR_UNSUPPORTED beyond these limits)          */
   int64_t head_dim;  /* d: 64 or 128                                       */
   int32_t causal;    /* 0 or 1 (key j visible to query i iff j <= i)       */
   int32_t dtype;     /* attn_dtype_t                                       */

@@ -57,6 +57,10 @@ attn_status_t check_problem(const attn_problem_t* prob, const void* q, const voi
                 (long long)prob->seq_len, (long long)kMaxSeq);
   if (prob->batch > 0 && prob->heads > INT32_MAX / prob->batch)
     return fail(ATTN_ERR_UNSUPPORTED, "batch*heads too large");
+  // the flash schedule numbers the 256-row query tiles of all heads in
+  // 32-bit arithmetic
+  if (prob->batch * prob->heads * ((prob->seq_len + 255) / 256) > (int64_t(1) << 30))
+    return fail(ATTN_ERR_UNSUPPORTED, "more than 2^30 query tiles of 256 rows");
   if (prob->causal != 0 && prob->causal != 1)
     return fail(ATTN_ERR_INVALID_ARG, "causal must be 0 or 1 (got %d)", prob->causal);
   if (prob->p_bf16 != 0 && prob->p_bf16 != 1)

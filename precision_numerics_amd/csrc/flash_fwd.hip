@@ -113,7 +113,60 @@ struct FlashParams {
   float scale_log2;  // softmax scale * log2(e)
   int p_round;       // fp32 P*V engines: round P to bf16 values first
   float beta;        // stabilised variant: normaliser factor for a repeated positive max
+  int64_t bh_count;  // batch * heads
+  int q_tiles;       // query tiles per (batch, head)
+  int64_t tiles;     // bh_count * q_tiles
+  int grp4;          // tile order in groups of four heads per XCD (bh_count % 32 == 0)
+  unsigned grid;     // workgroups: min(tiles, compute units)
 };
+
+// Tile schedule.  Logical tile L (0..tiles-1) is dispatched in an order
+// that keeps each head on one XCD (L % 8) and, with grp4, works on four
+// heads of an XCD at a time, longest causal query tiles first inside the
+// group: the K/V rows that concurrently resident workgroups re-read then fit
+// in the XCD's L2.  Workgroup w of a grid of P runs logical tiles
+// r*P + 8*jj + w%8 for rounds r = 0, 1, ..., where jj walks the XCD's
+// workgroups forward on even rounds and backward on odd ones: pairing long
+// and short causal tiles balances the work.  With P = tiles every
+// workgroup runs one tile.
+struct TileId {
+  int bh;      // batch * heads + head
+  int q0;      // first query row
+  int nblk;    // key blocks to visit
+  bool valid;
+};
+
+template <bool CAUSAL, int BC>
+__device__ __forceinline__ TileId tile_of(const FlashParams& p, int round) {
+  const uint32_t P = gridDim.x, w = blockIdx.x;
+  uint32_t L;
+  if (P % 8 == 0) {
+    const uint32_t J = P / 8, jw = w / 8;
+    const uint32_t jj = (round & 1) ? J - 1 - jw : jw;
+    L = (uint32_t)round * P + 8 * jj + w % 8;
+  } else {
+    L = (uint32_t)round * P + w;
+  }
+  TileId t;
+  t.valid = L < (uint32_t)p.tiles;
+  const uint32_t NT = (uint32_t)p.q_tiles;
+  uint32_t rank;  // 0 = the longest causal tile
+  if (p.grp4) {
+    const uint32_t x = L % 8, r = L / 8;
+    const uint32_t grp = r / (4 * NT), wi = r - grp * (4 * NT);
+    t.bh = (int)((grp * 4 + wi % 4) * 8 + x);
+    rank = wi / 4;
+  } else {
+    const uint32_t BHn = (uint32_t)p.bh_count;
+    rank = L / BHn;
+    t.bh = (int)(L - rank * BHn);
+  }
+  const int qt = CAUSAL ? (int)NT - 1 - (int)rank : (int)rank;
+  t.q0 = qt * kBR;
+  const int kend = CAUSAL ? min(p.n, t.q0 + kBR) : p.n;
+  t.nblk = t.valid ? (kend + BC - 1) / BC : 0;
+  return t;
+}
 
 // Key (0..31 inside a 32-key subtile) that row m of the K operand carries.
 __device__ __forceinline__ int key_of_row(int m) {
@@ -143,6 +196,16 @@ __device__ __forceinline__ float tree_max(const float (&x)[N]) {
 }
 
 template <bool B> struct BoolC { static constexpr bool value = B; };
+template <int I> struct IntC { static constexpr int value = I; };
+
+// f(IntC<0>{}), ..., f(IntC<N-1>{}): a loop whose index is a constant
+template <int N, int I = 0, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(IntC<I>{});
+    static_for<N, I + 1>(f);
+  }
+}
 
 // Ends the live range of a register value: the result is unspecified and
 // costs no instruction.  Used where a path leaves a value the program never
@@ -184,6 +247,11 @@ __device__ __forceinline__ i32x4 buffer_rsrc(const void* base, uint32_t bytes) {
   return i32x4{(int)(uint32_t)a, (int)(uint32_t)((a >> 32) & 0xffffu), (int)bytes, 0x00020000};
 }
 
+__device__ __forceinline__ i32x4 uniform(i32x4 x) {
+  return i32x4{__builtin_amdgcn_readfirstlane(x[0]), __builtin_amdgcn_readfirstlane(x[1]),
+               __builtin_amdgcn_readfirstlane(x[2]), __builtin_amdgcn_readfirstlane(x[3])};
+}
+
 // One wave-wide buffer load of 16 (or 4) bytes per lane straight into LDS at
 // lds_addr + 16*lane (4*lane).  Issued through inline asm on purpose: the
 // compiler's wait-count pass cannot tell which LDS bytes such a load writes,
@@ -191,19 +259,30 @@ __device__ __forceinline__ i32x4 buffer_rsrc(const void* base, uint32_t bytes) {
 // the prefetch.  Every wait these loads need is explicit in the kernel
 // (s_waitcnt vmcnt(0) before the barrier that publishes a tile); compiler-
 // generated waits for other memory operations only become more conservative.
+template <int IMM = 0>
 __device__ __forceinline__ void lds_load16(i32x4 rsrc, uint32_t voff, uint32_t soff,
-                                           uint32_t lds_addr) {
-  // M0 carries the LDS destination; it is declared clobbered, so the compiler
-  // re-establishes any value of its own after the load
+                                           uint32_t lds_base) {
+  // M0 carries the LDS destination, lds_base + IMM, formed inside the asm so
+  // the compiler keeps one base instead of one register per destination;
+  // M0 is declared clobbered, so the compiler re-establishes any value of
+  // its own after the load.  The scalar operands are wave-uniform; the
+  // read-first-lanes only tell the register allocator so (it may otherwise
+  // have moved a uniform value into vector registers).
+  rsrc = uniform(rsrc);
+  soff = __builtin_amdgcn_readfirstlane(soff);
+  lds_base = __builtin_amdgcn_readfirstlane(lds_base);
   asm volatile(
-      "s_mov_b32 m0, %3\n\ts_nop 0\n\t"
+      "s_add_u32 m0, %3, %4\n\ts_nop 0\n\t"
       "buffer_load_dwordx4 %0, %1, %2 offen lds"
       :
-      : "v"(voff), "s"(rsrc), "s"(soff), "s"(lds_addr)
-      : "memory", "m0");
+      : "v"(voff), "s"(rsrc), "s"(soff), "s"(lds_base), "i"(IMM)
+      : "memory", "m0", "scc");
 }
 __device__ __forceinline__ void lds_load4(i32x4 rsrc, uint32_t voff, uint32_t soff,
                                           uint32_t lds_addr) {
+  rsrc = uniform(rsrc);
+  soff = __builtin_amdgcn_readfirstlane(soff);
+  lds_addr = __builtin_amdgcn_readfirstlane(lds_addr);
   asm volatile(
       "s_mov_b32 m0, %3\n\ts_nop 0\n\t"
       "buffer_load_dword %0, %1, %2 offen lds"
@@ -274,13 +353,13 @@ __device__ __forceinline__ void issue_k(char* smem, int w, int lane, int kb, int
                                         const uint32_t* voffK) {
   using TL = Tile<D, QK, PV>;
   const i32x4 rsK = buffer_rsrc(kbase, (uint32_t)n * TL::kRowK);
-  const uint32_t base = lds_address(smem) + buf * TL::kBytesK;
-#pragma unroll
-  for (int i = 0; i < TL::kSegKPerWave; ++i) {
-    const int seg = w + i * TL::kIssuers;
-    if (TL::kSegK % TL::kIssuers == 0 || seg < TL::kSegK)
-      lds_load16(rsK, voffK[i], (uint32_t)kb * TL::kRowK, base + seg * 1024);
-  }
+  const uint32_t base = lds_address(smem) + buf * TL::kBytesK + w * 1024;
+  const uint32_t soff = (uint32_t)kb * TL::kRowK;
+  static_for<TL::kSegKPerWave>([&](auto ic) __attribute__((always_inline)) {
+    constexpr int i = decltype(ic)::value;
+    if (TL::kSegK % TL::kIssuers == 0 || w + i * TL::kIssuers < TL::kSegK)
+      lds_load16<i * TL::kIssuers * 1024>(rsK, voffK[i], soff, base);
+  });
   if constexpr (QK == QK_I8) {
     if (w == 0) {
       const i32x4 rsS = buffer_rsrc(sbase, (uint32_t)n * 4);
@@ -298,13 +377,13 @@ __device__ __forceinline__ void issue_v(char* smem, int w, int kb, int buf, cons
                                         int n, const uint32_t* voffV) {
   using TL = Tile<D, QK, PV>;
   const i32x4 rsV = buffer_rsrc(vbase, (uint32_t)n * TL::kRowV);
-  const uint32_t base = lds_address(smem) + TL::kOffV + buf * TL::kBytesV;
-#pragma unroll
-  for (int i = 0; i < TL::kSegVPerWave; ++i) {
-    const int seg = w + i * TL::kIssuers;
-    if (TL::kSegV % TL::kIssuers == 0 || seg < TL::kSegV)
-      lds_load16(rsV, voffV[i], (uint32_t)kb * TL::kRowV, base + seg * 1024);
-  }
+  const uint32_t base = lds_address(smem) + TL::kOffV + buf * TL::kBytesV + w * 1024;
+  const uint32_t soff = (uint32_t)kb * TL::kRowV;
+  static_for<TL::kSegVPerWave>([&](auto ic) __attribute__((always_inline)) {
+    constexpr int i = decltype(ic)::value;
+    if (TL::kSegV % TL::kIssuers == 0 || w + i * TL::kIssuers < TL::kSegV)
+      lds_load16<i * TL::kIssuers * 1024>(rsV, voffV[i], soff, base);
+  });
 }
 
 // Workgroup barrier without the memory fence that __syncthreads() carries.
@@ -325,12 +404,11 @@ __device__ __forceinline__ void block_barrier() {
 // The eight waves form two groups of four; group 1 runs one half-step
 // behind group 0, and every half-step ends at a workgroup barrier.  The two
 // waves sharing a SIMD therefore always run opposite half-steps: one keeps
-// the matrix cores busy while the other works the vector ALUs.
-// Buffers: K_j lives in K buffer j%2 and V_j in V buffer j%2.  At the start
-// of slot 2j the loads of K_{j+1} and V_j are issued (by every wave); they
-// are awaited at the end of slot 2j+1, so they land before slot 2j+2, the
-// first slot that reads them.  The buffers they overwrite were last read in
-// slot 2j-1.
+// the matrix cores busy while the other works the vector ALUs.  K and V
+// blocks are double-buffered in LDS (the slot loop below gives the exact
+// issue and wait points).  The kernel is persistent: a workgroup walks a
+// list of query tiles, and one tile's last slots overlap the next one's
+// first.
 template <int D, int QK, int PV, bool CAUSAL, bool DEBUG_S, bool STAB>
 __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
   using QT = typename QKTraits<QK>::T;
@@ -349,51 +427,58 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
   const int g = lane >> 5;
   const int n = lane & 31;
   const int N = p.n;
-  const int64_t bh = blockIdx.x;
-  const int tile = CAUSAL ? (int)(gridDim.y - 1 - blockIdx.y) : (int)blockIdx.y;
-  const int q0 = tile * kBR;
-  const int q0w = q0 + wave * 32;
-  const int qrow = q0w + n;
-  const bool qvalid = qrow < N;
-  const int64_t hoff = bh * (int64_t)N * D;
-  const QT* Qg = (const QT*)p.q + hoff;
+  const int wg = wave & (TL::kIssuers - 1);  // wave index inside its group
 
-  // ---- K/V streaming setup: per-lane source offsets of this wave's segments
-  const void* kbase = (const char*)p.k + hoff * (int64_t)sizeof(QT);
-  const void* vbase = (const char*)p.v + hoff * (int64_t)sizeof(VT);
-  const void* sbase = (QK == QK_I8) ? (const void*)(p.k_scale + bh * N) : nullptr;
+  // ---- the tile this workgroup works on (its identity changes at the
+  // switch to the next tile), and the next one
+  int round = 0;
+  TileId cur = tile_of<CAUSAL, BC>(p, 0);
+  TileId nxt = tile_of<CAUSAL, BC>(p, 1);
+  if (!cur.valid) return;  // never: the grid has at most `tiles` workgroups
+  int q0w = cur.q0 + wave * 32;
+  int qrow = q0w + n;
+  bool qvalid = qrow < N;
+  int bh = cur.bh;
+  auto head_ptr = [&](const void* base, int b, int esize) __attribute__((always_inline)) {
+    return (const void*)((const char*)base + (int64_t)b * N * D * esize);
+  };
+
   // group 0 holds the source offsets of its K segments, group 1 those of
   // its V segments, in the same registers
-  const int wg = wave & (TL::kIssuers - 1);  // wave index inside its group
   uint32_t voff[TL::kSegPerWave];
 #pragma unroll
   for (int i = 0; i < TL::kSegPerWave; ++i)
     voff[i] = group == 0 ? seg_src_offset(wg + i * TL::kIssuers, lane, TL::kRowK, TL::kStrK)
                          : seg_src_offset(wg + i * TL::kIssuers, lane, TL::kRowV, TL::kStrV);
 
-
   // The first K tile streams in while this lane's Q row loads.
-  if (group == 0) issue_k<D, QK, PV>(smem, wg, lane, 0, 0, kbase, sbase, N, voff);
+  if (group == 0)
+    issue_k<D, QK, PV>(smem, wg, lane, 0, 0, head_ptr(p.k, bh, sizeof(QT)),
+                       QK == QK_I8 ? (const void*)(p.k_scale + (int64_t)bh * N) : nullptr, N, voff);
 
   // ---- this lane's query row as the B operand of S^T = K Q^T (registers)
   constexpr int QST = (QK == QK_BF16) ? D / 16 : (QK == QK_I8 ? D / 32 : D / 2);
   i32x4 qv[QK == QK_F32 ? 1 : QST];
   float qf[QK == QK_F32 ? QST : 1];
   float sq_log2 = 0.f;
-  if constexpr (QK == QK_F32) {
+  // load the Q row of query `row` of head `b` (zeros past the sequence end)
+  auto load_q = [&](int b, int row) __attribute__((always_inline)) {
+    const bool ok = row < N;
+    const QT* Qg = (const QT*)p.q + (int64_t)b * N * D;
+    if constexpr (QK == QK_F32) {
 #pragma unroll
-    for (int t = 0; t < QST; ++t)
-      qf[t] = qvalid ? Qg[(int64_t)qrow * D + 2 * t + g] : 0.f;
-  } else {
-    constexpr int EPC = 16 / (int)sizeof(QT);  // elements per 16-byte chunk
+      for (int t = 0; t < QST; ++t) qf[t] = ok ? Qg[(int64_t)row * D + 2 * t + g] : 0.f;
+    } else {
+      constexpr int EPC = 16 / (int)sizeof(QT);  // elements per 16-byte chunk
 #pragma unroll
-    for (int t = 0; t < QST; ++t) {
-      const QT* src = Qg + (int64_t)qrow * D + 2 * EPC * t + EPC * g;
-      qv[t] = qvalid ? *(const i32x4*)src : i32x4{0, 0, 0, 0};
+      for (int t = 0; t < QST; ++t) {
+        const QT* src = Qg + (int64_t)row * D + 2 * EPC * t + EPC * g;
+        qv[t] = ok ? *(const i32x4*)src : i32x4{0, 0, 0, 0};
+      }
+      if constexpr (QK == QK_I8) sq_log2 = ok ? p.q_scale[(int64_t)b * N + row] * p.scale_log2 : 0.f;
     }
-    if constexpr (QK == QK_I8)
-      sq_log2 = qvalid ? p.q_scale[bh * N + qrow] * p.scale_log2 : 0.f;
-  }
+  };
+  load_q(bh, qrow);
 
   // One wait for the Q row and the first K tile, with a wait the compiler
   // sees: otherwise its wait-count pass, unsure the Q loads finished before
@@ -401,8 +486,6 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
   // every iteration, which would also drain the K/V prefetch.
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
-  const int kend = CAUSAL ? min(N, q0 + kBR) : N;
-  const int nblk = (kend + BC - 1) / BC;
   // Every wave runs all nblk blocks of its workgroup.  Near the causal
   // diagonal a block can lie entirely above a wave's rows: its scores are all
   // masked, so m and l are unchanged (exp(m - m') = 1) and P = 0 adds
@@ -437,27 +520,35 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
   // step is one straight-line region the scheduler can interleave: LDS reads
   // run a few matrix products ahead of their use, and the rescale of O is
   // spread over the products of the preceding d subtile.
-  // K loads a matrix half-step of group 0 issues for the next tile: key rows
-  // kb.. into K buffer buf, if on.
+  // Loads a matrix half-step issues for a following block (of this tile or
+  // of the next one): rows kb.. of the K (group 0) or V (group 1) head at
+  // base (and, for int8 K, its key scales at sbase) into buffer buf, if on.
   struct Prefetch {
+    const void* base;
+    const void* sbase;
     int kb, buf;
     bool on;
   };
-  const i32x4 rsK = buffer_rsrc(kbase, (uint32_t)N * TL::kRowK);
-  constexpr int NSEG = TL::kSegKPerWave;
-  // this wave's K segment q of the request
-  auto issue_one = [&](const int q, const Prefetch& rq) __attribute__((always_inline)) {
-    const int seg = wg + q * TL::kIssuers;
-    if (rq.on && (TL::kSegK % TL::kIssuers == 0 || seg < TL::kSegK))
-      lds_load16(rsK, voff[q], (uint32_t)rq.kb * TL::kRowK,
-                 lds_address(smem) + rq.buf * TL::kBytesK + seg * 1024);
+  // this wave's K segment q of a request
+  auto issue_one = [&](auto qc, const Prefetch& rq) __attribute__((always_inline)) {
+    constexpr int q = decltype(qc)::value;
+    if (rq.on && (TL::kSegK % TL::kIssuers == 0 || wg + q * TL::kIssuers < TL::kSegK))
+      lds_load16<q * TL::kIssuers * 1024>(
+          buffer_rsrc(rq.base, (uint32_t)N * TL::kRowK), voff[q], (uint32_t)rq.kb * TL::kRowK,
+          lds_address(smem) + rq.buf * TL::kBytesK + wg * 1024);
   };
 
-  auto m_body = [&](const int j, auto do_pv_c, auto do_s_c, auto issue_c,
+  auto m_body = [&](const int jl, const int jg, auto do_pv_c, auto do_s_c, auto issue_c,
                     const Prefetch& rq) __attribute__((always_inline)) {
     constexpr bool DO_PV = decltype(do_pv_c)::value;
     constexpr bool DO_S = decltype(do_s_c)::value;
-    constexpr bool ISSUE = decltype(issue_c)::value;
+    // loads to issue: 0 none, 1 K (spread over the products), 2 V (all
+    // before the first product)
+    constexpr int ISSUE = decltype(issue_c)::value;
+    constexpr int NSEG = TL::kSegKPerWave;
+    if constexpr (ISSUE == 2) {
+      if (rq.on) issue_v<D, QK, PV>(smem, wg, rq.kb, rq.buf, rq.base, N, voff);
+    }
     if constexpr (PV == PV_BF16 && QK == QK_BF16) {
       // The whole half-step in program order, fenced so that the scheduler
       // keeps it: product i is followed by the LDS reads of product
@@ -472,8 +563,8 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
       constexpr int kAhead = 8;
       constexpr int NPV = DO_PV ? DT * (BC / 16) : 0;  // P.V products, u-major
       constexpr int NSM = DO_S ? NKS * QST : 0;        // S products, chain by chain
-      const char* vl = (const char*)smem + TL::kOffV + ((j - 1) & 1) * TL::kBytesV + v_lane;
-      const char* k0 = (const char*)smem + (j & 1) * TL::kBytesK + k_lane + 16 * g;
+      const char* vl = (const char*)smem + TL::kOffV + ((jg - 1) & 1) * TL::kBytesV + v_lane;
+      const char* k0 = (const char*)smem + (jg & 1) * TL::kBytesK + k_lane + 16 * g;
       i16x4 vlo[NPV > 0 ? NPV : 1], vhi[NPV > 0 ? NPV : 1];
       i32x4 kf[NSM > 0 ? NSM : 1];
       f32x16 acc[NKS];
@@ -509,10 +600,11 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
         __builtin_amdgcn_sched_barrier(0);
         product(i);
         if (i + kAhead < NPV + NSM) load(i + kAhead);
-        if constexpr (ISSUE) {
-#pragma unroll
-          for (int q = 0; q < NSEG; ++q)
-            if ((2 * q + 1) * (NPV + NSM) / (2 * NSEG) == i) issue_one(q, rq);
+        if constexpr (ISSUE == 1) {
+          static_for<NSEG>([&](auto qc) __attribute__((always_inline)) {
+            constexpr int q = decltype(qc)::value;
+            if ((2 * q + 1) * (NPV + NSM) / (2 * NSEG) == i) issue_one(qc, rq);
+          });
         }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -535,11 +627,11 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
           else forget(s[ks][r]);
         }
     } else {
-      if constexpr (ISSUE) {
-        if (rq.on) issue_k<D, QK, PV>(smem, wg, lane, rq.kb, rq.buf, kbase, sbase, N, voff);
+      if constexpr (ISSUE == 1) {
+        if (rq.on) issue_k<D, QK, PV>(smem, wg, lane, rq.kb, rq.buf, rq.base, rq.sbase, N, voff);
       }
       if constexpr (DO_PV) {
-        const char* vt = (const char*)smem + TL::kOffV + ((j - 1) & 1) * TL::kBytesV;
+        const char* vt = (const char*)smem + TL::kOffV + ((jg - 1) & 1) * TL::kBytesV;
         if constexpr (PV == PV_BF16) {
           // key-group-outer order: P_{j-1} registers die group by group, so
           // they are gone before the new scores are born
@@ -587,7 +679,7 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
           for (int r = 0; r < 16; ++r) forget(s[ks][r]);
       }
       if constexpr (DO_S) {
-        const char* kt = (const char*)smem + (j & 1) * TL::kBytesK;
+        const char* kt = (const char*)smem + (jg & 1) * TL::kBytesK;
         if constexpr (QK == QK_BF16) {
           f32x16 acc[NKS];
 #pragma unroll
@@ -609,7 +701,7 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) s[ks][r] = acc[ks][r];  // raw q.k; scaled inside exp2
         } else if constexpr (QK == QK_I8) {
-          const float* skt = (const float*)(smem + TL::kOffSk + (j & 1) * TL::kBytesSk);
+          const float* skt = (const float*)(smem + TL::kOffSk + (jg & 1) * TL::kBytesSk);
 #pragma unroll
           for (int ks = 0; ks < NKS; ++ks) {
             const char* krow = kt + ks * 32 * TL::kStrK + k_lane + 16 * g;
@@ -619,10 +711,10 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
               acc = mfma_i8(*(const i32x4*)(krow + 32 * st), qv[st], acc);
             if constexpr (DEBUG_S) {
               if (qvalid) {
-                int32_t* dst = p.s_dbg + (bh * N + qrow) * (int64_t)N;
+                int32_t* dst = p.s_dbg + ((int64_t)bh * N + qrow) * (int64_t)N;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                  const int key = j * BC + 32 * ks + key_of_reg(r, g);
+                  const int key = jl * BC + 32 * ks + key_of_reg(r, g);
                   if (key < N) dst[key] = acc[r];
                 }
               }
@@ -655,21 +747,36 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
     // visible are left alone, wholly invisible ones are set to -inf, and
     // only a subtile the diagonal or the sequence end crosses is masked
     // element by element.
-    const bool need_mask = (kb + BC > N) || (CAUSAL && kb + BC - 1 > q0w);
+    // Without the causal mask the diagonal row is N (no key lies beyond
+    // it), kept opaque so that both variants compile to the same code
+    // shape (the optimiser's own specialisation of the non-causal one
+    // spills registers).
+    int diag0 = CAUSAL ? q0w : N;  // first query row of this wave
+    int diag = CAUSAL ? qrow : N;  // this lane's query row
+    asm volatile("" : "+s"(diag0), "+v"(diag));
+    const bool need_mask = (kb + BC > N) || (kb + BC - 1 > diag0);
     if (need_mask) {
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
         const int k0s = kb + 32 * ks;
-        const bool all_vis = (k0s + 31 < N) && (!CAUSAL || k0s + 31 <= q0w);
-        const bool none_vis = (k0s >= N) || (CAUSAL && k0s > q0w + 31);
+        const bool all_vis = (k0s + 31 < N) && (k0s + 31 <= diag0);
+        const bool none_vis = (k0s >= N) || (k0s > diag0 + 31);
         if (none_vis) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) s[ks][r] = -INFINITY;
         } else if (!all_vis) {
+          // key of register r = k0s + 8g + c_r with c_r = 16(r/8) + r%8: the
+          // tests compare the constant c_r with per-lane thresholds
+          int lim_diag = diag - k0s - 8 * g;  // visible iff c_r <= lim_diag
+          int lim_end = N - k0s - 8 * g;      // in range iff c_r < lim_end
+          // opaque to the optimiser: otherwise it hoists the sixteen
+          // compares of each subtile out of the loop as lane masks held in
+          // scalar registers
+          asm volatile("" : "+v"(lim_diag), "+v"(lim_end));
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int key = k0s + key_of_reg(r, g);
-            if (key >= N || (CAUSAL && key > qrow)) s[ks][r] = -INFINITY;
+            const int c = 16 * (r >> 3) + (r & 7);
+            if (c >= lim_end || c > lim_diag) s[ks][r] = -INFINITY;
           }
         }
       }
@@ -750,91 +857,162 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
     if constexpr (STAB) pin(nmax_run);
   };
 
-  // Group 0 runs slots (M_j, X_j) = (2j, 2j+1); group 1 runs (M_j, X_j) in
-  // slots (2j+1, 2j+2) after an idle slot 0.  Both pass exactly 2*nblk + 2
-  // barriers.  Group 0 issues the loads of K_{j+1} during M_j (slot 2j),
-  // group 1 those of V_j at the start of slot 2j; each group awaits its own
-  // loads at the end of slot 2j+1, before slot 2j+2, the first that reads
-  // them.  The buffers they overwrite were last read in slot 2j-1.  M_0 has
-  // no P.V part and M_nblk no S part; they are peeled off the loop, whose
-  // body is the full step.
+  // ---- epilogue of a finished tile: O = O^T / l, stored row-major, and the
+  // optional log-sum-exp; then the running state restarts for the next tile
+  auto finish = [&](int b, int row) __attribute__((always_inline)) {
+    const float l_tot = pair32_sum(l_run);
+    const float inv = 1.f / l_tot;
+    if (row < N) {
+      VT* dst = (VT*)p.o + (int64_t)b * N * D + (int64_t)row * D;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int b4 = 0; b4 < 4; ++b4) {
+          const int d0 = 32 * dt + 8 * b4 + 4 * g;
+          const float x0 = oacc[dt][4 * b4 + 0] * inv, x1 = oacc[dt][4 * b4 + 1] * inv;
+          const float x2 = oacc[dt][4 * b4 + 2] * inv, x3 = oacc[dt][4 * b4 + 3] * inv;
+          if constexpr (sizeof(VT) == 2) {
+            uint2 w;
+            w.x = (uint32_t)f32_to_bf16(x0) | ((uint32_t)f32_to_bf16(x1) << 16);
+            w.y = (uint32_t)f32_to_bf16(x2) | ((uint32_t)f32_to_bf16(x3) << 16);
+            *(uint2*)(dst + d0) = w;
+          } else {
+            *(float4*)(dst + d0) = make_float4(x0, x1, x2, x3);
+          }
+        }
+      if (p.lse != nullptr && g == 0) p.lse[(int64_t)b * N + row] = (m_run + __log2f(l_tot)) * kLn2;
+    }
+    m_run = -INFINITY;
+    mraw_run = -INFINITY;
+    l_run = 0.f;
+    nmax_run = 0;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x16{};
+  };
+
+  // Slots.  Each group runs, tile after tile, the sequence
+  //     M_0 X_0 M_1 X_1 ... M_{n-1} X_{n-1} M_n
+  // (2n+1 slots, one workgroup barrier each; M_0 has no P.V part, M_n no S
+  // part), group 1 one slot behind group 0: the two waves of a SIMD always
+  // run opposite half-steps, except at a tile switch, where group 1's M_n
+  // (P.V only) meets group 0's M_0 of the next tile (S only) -- the two
+  // together are one full step of matrix work.  Group 1 starts with an idle
+  // slot and group 0 ends with one, so both pass the same barriers.
+  //
+  // Blocks are numbered globally across the workgroup's tiles (jg); block
+  // jg's K and V sit in buffers jg%2.  Only matrix half-steps issue loads:
+  // group 0 issues the K loads of block jg+1 spread over its M of block jg
+  // and awaits them at the end of the following X; group 1 issues the V
+  // loads of block jg at the start of its M of block jg and awaits them at
+  // the end of that M.  Either way the loads land before the first slot
+  // that reads them, and the buffer they overwrite was last read in the
+  // slot before the issuing one.  (Issued from the vector half-steps
+  // instead, the loads measurably slow the kernel down.)  The next
+  // tile's first K block continues this numbering, and its Q rows are
+  // loaded at the start of X_{n-1}, after the last S products of the
+  // current tile read Q.  A finished tile's O is stored at the start of the
+  // next tile's X_0 (O, l and m are not touched by M_0).
   constexpr BoolC<true> kYes{};
   constexpr BoolC<false> kNo{};
-  const Prefetch kNone{0, 0, false};
+  constexpr IntC<0> kIssueNone{};
+  constexpr IntC<1> kIssueK{};
+  constexpr IntC<2> kIssueV{};
+  const Prefetch kNone{nullptr, nullptr, 0, 0, false};
+  int jg0 = 0;             // global number of the current tile's first block
+  bool pending = false;    // a finished tile's O waits in the registers
+  int pend_bh = 0;
+  int pend_row = 0;
+  // the K (or V) block following local block j of the current tile
+  auto next_k = [&](int j) __attribute__((always_inline)) {
+    const bool same = j + 1 < cur.nblk;
+    const int b = same ? cur.bh : nxt.bh;
+    return Prefetch{head_ptr(p.k, b, sizeof(QT)),
+                    QK == QK_I8 ? (const void*)(p.k_scale + (int64_t)b * N) : nullptr,
+                    same ? (j + 1) * BC : 0, (jg0 + j + 1) & 1, same || nxt.valid};
+  };
+  // the V block of local block j of the current tile
+  auto this_v = [&](int j) __attribute__((always_inline)) {
+    return Prefetch{head_ptr(p.v, cur.bh, sizeof(VT)), nullptr, j * BC, (jg0 + j) & 1, true};
+  };
+  // start of X_j: the finished tile's output, the next tile's Q rows
+  auto x_prologue = [&](int j) __attribute__((always_inline)) {
+    if (j == 0 && pending) {
+      finish(pend_bh, pend_row);
+      pending = false;
+    }
+    if (j == cur.nblk - 1 && nxt.valid) load_q(nxt.bh, nxt.q0 + wave * 32 + n);
+  };
+  // after M_n: the next tile becomes current
+  auto advance = [&]() __attribute__((always_inline)) {
+    pending = true;
+    pend_bh = bh;
+    pend_row = qrow;
+    jg0 += cur.nblk;
+    cur = nxt;
+    ++round;
+    nxt = tile_of<CAUSAL, BC>(p, round + 1);
+    bh = cur.bh;
+    q0w = cur.q0 + wave * 32;
+    qrow = q0w + n;
+    qvalid = qrow < N;
+  };
+
   if (group == 0) {
-    // slots 0, 1
-    m_body(0, kNo, kYes, kYes, Prefetch{BC, 1, 1 < nblk});
-    block_barrier();
-    half_x(0);
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    block_barrier();
-    for (int j = 1; j < nblk; ++j) {
-      // slots 2j, 2j+1
-      m_body(j, kYes, kYes, kYes, Prefetch{(j + 1) * BC, (j + 1) & 1, j + 1 < nblk});
+    while (true) {
+      m_body(0, jg0, kNo, kYes, kIssueK, next_k(0));
       block_barrier();
-      half_x(j);
+      x_prologue(0);
+      half_x(0);
       __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
       block_barrier();
+      for (int j = 1; j < cur.nblk; ++j) {
+        m_body(j, jg0 + j, kYes, kYes, kIssueK, next_k(j));
+        block_barrier();
+        x_prologue(j);
+        half_x(j);
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        block_barrier();
+      }
+      m_body(cur.nblk, jg0 + cur.nblk, kYes, kNo, kIssueNone, kNone);
+      block_barrier();
+      const bool more = nxt.valid;
+      advance();
+      if (!more) break;
     }
-    // slots 2 nblk, 2 nblk + 1
-    m_body(nblk, kYes, kNo, kNo, kNone);
-    block_barrier();
+    finish(pend_bh, pend_row);
     block_barrier();
   } else {
-    // slot 0
-    issue_v<D, QK, PV>(smem, wg, 0, 0, vbase, N, voff);
     block_barrier();
-    // slots 1, 2
-    m_body(0, kNo, kYes, kNo, kNone);
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    block_barrier();
-    if (1 < nblk) issue_v<D, QK, PV>(smem, wg, BC, 1, vbase, N, voff);
-    half_x(0);
-    block_barrier();
-    for (int j = 1; j < nblk; ++j) {
-      // slots 2j+1, 2j+2
-      m_body(j, kYes, kYes, kNo, kNone);
+    while (true) {
+      m_body(0, jg0, kNo, kYes, kIssueV, this_v(0));
       __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
       block_barrier();
-      if (j + 1 < nblk) issue_v<D, QK, PV>(smem, wg, (j + 1) * BC, (j + 1) & 1, vbase, N, voff);
-      half_x(j);
+      x_prologue(0);
+      half_x(0);
       block_barrier();
-    }
-    // slot 2 nblk + 1
-    m_body(nblk, kYes, kNo, kNo, kNone);
-    block_barrier();
-  }
-
-  // ---- epilogue: O = O^T / l, stored row-major; optional log-sum-exp
-  const float l_tot = pair32_sum(l_run);
-  const float inv = 1.f / l_tot;
-  if (qvalid) {
-    VT* dst = (VT*)p.o + hoff + (int64_t)qrow * D;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int b4 = 0; b4 < 4; ++b4) {
-        const int d0 = 32 * dt + 8 * b4 + 4 * g;
-        const float x0 = oacc[dt][4 * b4 + 0] * inv, x1 = oacc[dt][4 * b4 + 1] * inv;
-        const float x2 = oacc[dt][4 * b4 + 2] * inv, x3 = oacc[dt][4 * b4 + 3] * inv;
-        if constexpr (sizeof(VT) == 2) {
-          uint2 w;
-          w.x = (uint32_t)f32_to_bf16(x0) | ((uint32_t)f32_to_bf16(x1) << 16);
-          w.y = (uint32_t)f32_to_bf16(x2) | ((uint32_t)f32_to_bf16(x3) << 16);
-          *(uint2*)(dst + d0) = w;
-        } else {
-          *(float4*)(dst + d0) = make_float4(x0, x1, x2, x3);
-        }
+      for (int j = 1; j < cur.nblk; ++j) {
+        m_body(j, jg0 + j, kYes, kYes, kIssueV, this_v(j));
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        block_barrier();
+        x_prologue(j);
+        half_x(j);
+        block_barrier();
       }
-    if (p.lse != nullptr && g == 0)
-      p.lse[bh * N + qrow] = (m_run + __log2f(l_tot)) * kLn2;
+      m_body(cur.nblk, jg0 + cur.nblk, kYes, kNo, kIssueNone, kNone);
+      block_barrier();
+      const bool more = nxt.valid;
+      advance();
+      if (!more) break;
+    }
+    finish(pend_bh, pend_row);
   }
 }
 
 template <int D, int QK, int PV, bool CAUSAL, bool DEBUG_S, bool STAB>
 hipError_t launch_t(const FlashParams& fp, int64_t bh, int ntiles, hipStream_t st) {
-  dim3 grid((unsigned)bh, (unsigned)ntiles, 1);
-  hipLaunchKernelGGL((flash_fwd_kernel<D, QK, PV, CAUSAL, DEBUG_S, STAB>), grid,
+  (void)bh;
+  (void)ntiles;
+  hipLaunchKernelGGL((flash_fwd_kernel<D, QK, PV, CAUSAL, DEBUG_S, STAB>), dim3(fp.grid),
                      dim3(kThreads), 0, st, fp);
   return hipGetLastError();
 }
@@ -886,6 +1064,18 @@ hipError_t launch_flash(const AttnArgs& a, hipStream_t stream) {
   fp.beta = a.beta;
   const int64_t bh = a.batch * a.heads;
   const int ntiles = (int)((a.seq_len + kBR - 1) / kBR);
+  fp.bh_count = bh;
+  fp.q_tiles = ntiles;
+  fp.tiles = bh * ntiles;
+  // one workgroup per compute unit (the LDS footprint allows no second),
+  // each walking its share of the tiles
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  fp.grid = (unsigned)(fp.tiles < (int64_t)cus ? fp.tiles : (int64_t)cus);
+  fp.grp4 = (bh % 32 == 0 && fp.grid % 8 == 0) ? 1 : 0;
   if (a.head_dim == 64) return launch_d<64>(a, fp, bh, ntiles, stream);
   if (a.head_dim == 128) return launch_d<128>(a, fp, bh, ntiles, stream);
   return hipErrorInvalidValue;

@@ -53,6 +53,7 @@ FAKE = 0x1000  # never dereferenced: every case below fails validation first
     (dict(head_dim=0), B.ATTN_ERR_INVALID_ARG),
     (dict(batch=-1), B.ATTN_ERR_INVALID_ARG),
     (dict(seq_len=(1 << 22) + 1), B.ATTN_ERR_UNSUPPORTED),
+    (dict(batch=1 << 16, heads=1 << 8, seq_len=1 << 22), B.ATTN_ERR_UNSUPPORTED),  # tiles
     (dict(causal=2), B.ATTN_ERR_INVALID_ARG),
     (dict(p_bf16=7), B.ATTN_ERR_INVALID_ARG),
     (dict(dtype=9), B.ATTN_ERR_INVALID_ARG),
