@@ -47,9 +47,9 @@ TRAFFIC_SOURCES = ("precision_numerics_amd/csrc/flash_fwd.hip",
                    "precision_numerics_amd/csrc/launch.hpp")
 TRAFFIC = {
     "workload": "c3",
-    "sources_sha256": "7e8db7f29e88cec0cce02e70b880e70cd60942db7cdcc3e16aba54471de3356d",
-    "fetch_kib": 676981.0, "fetch_scale": 2.0,
-    "write_kib": 131072.0, "write_scale": 1.0,
+    "sources_sha256": "ac649a5af85f77a007153c8a7dbb2613f2d2673694ddbd456018fb0b252e7296",
+    "fetch_kib": 293265.2, "fetch_scale": 2.0,
+    "write_kib": 135936.8, "write_scale": 1.0,
 }
 
 
