@@ -8,7 +8,9 @@ from .attention import (default_scale, attention, attention_head, int8_scores,
                         attention_int8, attention_int8_head, quantize_int8,
                         deviation, attention_probabilities, attention_delta,
                         run_heads)
+from .distance import wasserstein, wasserstein1_cdf
 
 __all__ = ["default_scale", "attention", "attention_head", "int8_scores",
            "attention_int8", "attention_int8_head", "quantize_int8",
-           "deviation", "attention_probabilities", "attention_delta", "run_heads"]
+           "deviation", "attention_probabilities", "attention_delta", "run_heads",
+           "wasserstein", "wasserstein1_cdf"]

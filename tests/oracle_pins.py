@@ -374,3 +374,91 @@ def check_delta(ora):
         p = ora.attention_probabilities(q, k, causal=causal, scale=0.5)
         via_p = (p * (d_o @ v.T)).sum(axis=1)
         assert np.allclose(ora.attention_delta(out, d_o), via_p, rtol=1e-12, atol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# Wasserstein distances between empirical distributions
+# ---------------------------------------------------------------------------
+
+def _brute_force_w(u, v):
+    """Optimal transport between two uniform samples of equal size by
+    enumeration of every pairing: W_1, W_2, W_inf."""
+    import itertools
+    n = len(u)
+    best1 = best2 = bestinf = math.inf
+    for perm in itertools.permutations(range(n)):
+        gaps = [abs(u[i] - v[perm[i]]) for i in range(n)]
+        best1 = min(best1, math.fsum(gaps) / n)
+        best2 = min(best2, math.fsum(g * g for g in gaps) / n)
+        bestinf = min(bestinf, max(gaps))
+    return best1, math.sqrt(best2), bestinf
+
+
+def _lp_transport(u, v, power):
+    """min sum_ij |u_i - v_j|^power g_ij over couplings g of the uniform
+    distributions on u (n atoms) and v (m atoms): the transport linear
+    program, solved by scipy's HiGHS."""
+    from scipy.optimize import linprog
+    n, m = len(u), len(v)
+    cost = np.abs(np.subtract.outer(np.asarray(u), np.asarray(v))) ** power
+    a_eq = np.zeros((n + m, n * m))
+    for i in range(n):
+        a_eq[i, i * m:(i + 1) * m] = 1.0
+    for j in range(m):
+        a_eq[n + j, j::m] = 1.0
+    b_eq = np.concatenate((np.full(n, 1.0 / n), np.full(m, 1.0 / m)))
+    res = linprog(cost.ravel(), A_eq=a_eq, b_eq=b_eq, bounds=(0, None), method="highs")
+    assert res.status == 0
+    return res.fun
+
+
+@pin
+def check_wasserstein(ora):
+    """W_p from the quantile functions against: enumeration of every pairing
+    (equal sizes, with ties), the transport linear program (unequal sizes),
+    the distribution-function area formula and scipy for p = 1, and closed
+    forms (point masses, a two-point law, shifts, scaling, symmetry)."""
+    rng = _rng(51)
+    for n in range(1, 7):
+        for trial in range(3):
+            u = rng.standard_normal(n).round(1 if trial == 2 else 12)
+            v = rng.standard_normal(n).round(1 if trial == 2 else 12)
+            w = ora.wasserstein(u, v)
+            b1, b2, binf = _brute_force_w(list(u), list(v))
+            assert abs(w["w1"] - b1) <= 1e-12 and abs(w["w2"] - b2) <= 1e-12, (w, b1, b2)
+            assert w["winf"] == binf and w["n_nonfinite"] == 0
+    for n, m in ((1, 3), (2, 3), (3, 5), (4, 6), (7, 2)):
+        u = rng.standard_normal(n)
+        v = rng.standard_normal(m) * 2.0 + 0.3
+        w = ora.wasserstein(u, v)
+        assert abs(w["w1"] - _lp_transport(u, v, 1)) <= 1e-9
+        assert abs(w["w2"] ** 2 - _lp_transport(u, v, 2)) <= 1e-9
+        assert abs(w["w1"] - ora.wasserstein1_cdf(u, v)) <= 1e-12
+    from scipy.stats import wasserstein_distance
+    for n, m in ((50, 50), (37, 91), (500, 3)):
+        u = rng.standard_normal(n) ** 3
+        v = rng.gamma(2.0, size=m) - 1.0
+        ref = wasserstein_distance(u, v)
+        assert abs(ora.wasserstein(u, v)["w1"] - ref) <= 1e-12 * max(1.0, ref)
+        assert abs(ora.wasserstein1_cdf(u, v) - ref) <= 1e-12 * max(1.0, ref)
+    # closed forms
+    w = ora.wasserstein([2.5], [-1.0])
+    assert w["w1"] == 3.5 and w["w2"] == 3.5 and w["winf"] == 3.5
+    w = ora.wasserstein([0.0, 1.0], [0.0])
+    assert w["w1"] == 0.5 and abs(w["w2"] - math.sqrt(0.5)) <= 1e-15 and w["winf"] == 1.0
+    assert ora.wasserstein1_cdf([0.0, 1.0], [0.0]) == 0.5
+    u = rng.standard_normal(1000)
+    w = ora.wasserstein(u, u + 0.75)       # a shift moves every quantile by 0.75
+    for key in ("w1", "w2", "winf"):
+        assert abs(w[key] - 0.75) <= 1e-12
+    w0 = ora.wasserstein(u, rng.permutation(u))
+    assert w0["w1"] == 0.0 and w0["winf"] == 0.0
+    v = rng.standard_normal(700)
+    a, b = ora.wasserstein(u, v), ora.wasserstein(v, u)
+    c = ora.wasserstein(-3.0 * u, -3.0 * v)
+    for key in ("w1", "w2", "winf"):
+        assert abs(a[key] - b[key]) <= 1e-15 * max(1.0, a[key])
+        assert abs(c[key] - 3.0 * a[key]) <= 1e-12 * max(1.0, a[key])
+    # non-finite inputs
+    w = ora.wasserstein([1.0, float("nan"), float("inf")], [0.0, 1.0, 2.0])
+    assert w["n_nonfinite"] == 2 and math.isnan(w["w1"]) and math.isnan(w["winf"])

@@ -9,8 +9,9 @@ import pytest
 
 import oracle_pins
 
-SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
-                   "oracle", "attention.py")
+ORACLE_DIR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle")
+SRC = os.path.join(ORACLE_DIR, "attention.py")
+DIST_SRC = os.path.join(ORACLE_DIR, "distance.py")
 
 MUTANTS = [
     ("diagonal dropped from causal mask", "return cols <= rows", "return cols < rows"),
@@ -71,17 +72,43 @@ MUTANTS = [
 ]
 
 
-def _mutant_module(old, new):
-    src = open(SRC).read()
-    assert src.count(old) == 1, f"mutation site not unique: {old!r}"
+DIST_MUTANTS = [
+    ("quantiles not sorted", "return np.sort(a), bad", "return a, bad"),
+    ("quantile index one late", "ia = -(-ends // m) - 1", "ia = np.minimum(-(-ends // m), n - 1)"),
+    ("quantile indices from the wrong size", "ib = -(-ends // n) - 1", "ib = -(-ends // m) - 1"),
+    ("interval widths dropped", "w1 = float((width * gap).sum())", "w1 = float(gap.mean())"),
+    ("W2 without root", "w2 = float(math.sqrt((width * gap * gap).sum()))",
+     "w2 = float((width * gap * gap).sum())"),
+    ("W_inf as a mean", "winf = float(gap.max())", "winf = float(gap.mean())"),
+    ("intervals start one step late", "starts = np.concatenate(([0], ends[:-1]))",
+     "starts = np.concatenate(([0, 0], ends[:-2]))"),
+    ("CDF counts strictly below", 'fa = np.searchsorted(a, z[:-1], side="right") / a.size',
+     'fa = np.searchsorted(a, z[:-1], side="left") / a.size'),
+    ("CDF difference without abs", "return float((np.diff(z) * np.abs(fa - fb)).sum())",
+     "return float((np.diff(z) * (fa - fb)).sum())"),
+    ("non-finite values ignored", "bad = int((~np.isfinite(a)).sum())", "bad = 0"),
+]
+
+
+def _mutant_module(old, new, path=SRC):
+    """The oracle's two modules in one namespace, one of them mutated."""
     mod = types.ModuleType("oracle_mutant")
-    exec(compile(src.replace(old, new), SRC + " (mutant)", "exec"), mod.__dict__)
+    for src_path in (SRC, DIST_SRC):
+        src = open(src_path).read()
+        if src_path == path:
+            assert src.count(old) == 1, f"mutation site not unique: {old!r}"
+            src = src.replace(old, new)
+        exec(compile(src, src_path + " (mutant)", "exec"), mod.__dict__)
     return mod
 
 
-@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
-def test_pins_catch_mutant(name, old, new):
-    mod = _mutant_module(old, new)
+ALL_MUTANTS = [(n, o, w, SRC) for n, o, w in MUTANTS] + \
+              [(n, o, w, DIST_SRC) for n, o, w in DIST_MUTANTS]
+
+
+@pytest.mark.parametrize("name,old,new,path", ALL_MUTANTS, ids=[m[0] for m in ALL_MUTANTS])
+def test_pins_catch_mutant(name, old, new, path):
+    mod = _mutant_module(old, new, path)
     caught = []
     for check in oracle_pins.PINS:
         try:
@@ -93,5 +120,8 @@ def test_pins_catch_mutant(name, old, new):
 
 def test_unmutated_copy_passes_all_pins():
     mod = _mutant_module("def default_scale", "def default_scale")
+    for check in oracle_pins.PINS:
+        check(mod)
+    mod = _mutant_module("def wasserstein(", "def wasserstein(", DIST_SRC)
     for check in oracle_pins.PINS:
         check(mod)
