@@ -336,6 +336,7 @@ def main():
     # ---- other kernels of the path, each timed alone
     if not args.no_legs:
         legs = {}
+        ob_s = None
         try:
             log("bench: baseline attention leg")
             prob = pna.make_problem(q, causal=cfg.causal, p_bf16=p_bf16)
@@ -375,6 +376,27 @@ def main():
                                      "note": "includes the host synchronisation per call"}
             except Exception as exc:                     # noqa: BLE001
                 legs["deviation"] = {"error": repr(exc)}
+        if ref_t is not None:
+            try:
+                log("bench: Wasserstein leg")
+                ws_b = torch.empty(pna.attn_wasserstein_scratch_size(
+                    ref_t.numel(), pna.ATTN_BF16 if o_s.dtype == torch.bfloat16 else pna.ATTN_F32,
+                    pna.ATTN_F64), dtype=torch.uint8, device="cuda")
+                wf = pna.attn_wasserstein(o_s, ref_t, scratch=ws_b)
+                wms = event_time_ms(lambda: pna.attn_wasserstein(o_s, ref_t, scratch=ws_b), 3, 1)
+                leg = {"flash_vs_fp64": {k2: wf[k2] for k2 in ("w1", "w2", "winf")},
+                       "ms": round(wms, 3), "n": wf["n"],
+                       "note": "one call sorts both inputs on the GPU; includes the host "
+                               "synchronisation"}
+                if ob_s is not None:
+                    wb = pna.attn_wasserstein(ob_s, ref_t, scratch=ws_b)
+                    wfb = pna.attn_wasserstein(o_s, ob_s)
+                    leg["baseline_vs_fp64"] = {k2: wb[k2] for k2 in ("w1", "w2", "winf")}
+                    leg["flash_vs_baseline"] = {k2: wfb[k2] for k2 in ("w1", "w2", "winf")}
+                legs["wasserstein"] = leg
+                del ws_b
+            except Exception as exc:                     # noqa: BLE001
+                legs["wasserstein"] = {"error": repr(exc)}
         if bias_refs is not None:
             try:
                 log("bench: rounding-bias leg (c4, standard vs stabilised)")

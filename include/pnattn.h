@@ -23,8 +23,8 @@
  *    device memory and keeps no state besides a thread-local error string.
  *  - stream is a hipStream_t passed as void* (NULL = the default stream).
  *    Calls enqueue work and return; kernel faults surface at the caller's
- *    next synchronisation.  attn_deviation is the exception: it synchronises
- *    its stream before it returns.
+ *    next synchronisation.  attn_deviation and attn_wasserstein are the
+ *    exceptions: they synchronise their stream before they return.
  *  - Validation is pure host code and runs before any HIP call: on an error
  *    nothing is launched and no output is touched.  attn_last_error() then
  *    describes the failure.
@@ -50,8 +50,9 @@ typedef enum {
 typedef enum {
   ATTN_F32 = 0,  /* Q, K, V and O are fp32                                 */
   ATTN_BF16 = 1, /* Q, K, V and O are bf16                                 */
-  ATTN_INT8 = 2  /* Q, K are int8 codes with fp32 per-row scales;
+  ATTN_INT8 = 2, /* Q, K are int8 codes with fp32 per-row scales;
                     V and O are bf16                                        */
+  ATTN_F64 = 3   /* fp64 values: only as an input of attn_wasserstein      */
 } attn_dtype_t;
 
 typedef struct {
@@ -158,6 +159,40 @@ attn_status_t attn_deviation(const void* o_test, int32_t o_dtype,
                              const double* o_ref, int64_t n, void* scratch,
                              size_t scratch_bytes, attn_deviation_t* out_host,
                              void* stream);
+
+/* Wasserstein distances between the empirical distributions of two tensors
+ * of n values each ("Is Flash Attention Stable?", abstract: the impact of
+ * numeric deviation measured with the Wasserstein distance, after
+ * "Statistical Aspects of Wasserstein Distances" in its reference list).
+ * Each tensor is the uniform distribution on its n values; on the real line
+ * the optimal coupling pairs equal order statistics a_(i), b_(i), so
+ *   w1   = sum_i |a_(i) - b_(i)| / n
+ *   w2   = sqrt(sum_i (a_(i) - b_(i))^2 / n)
+ *   winf = max_i |a_(i) - b_(i)|
+ * computed in fp64 from the exact values, in a fixed order (bitwise
+ * reproducible).  If either tensor holds a NaN or an infinity the three
+ * distances are NaN and n_nonfinite counts those elements.               */
+typedef struct {
+  double w1, w2, winf;
+  int64_t n, n_nonfinite;
+} attn_wasserstein_t;
+
+/* Bytes of device scratch attn_wasserstein needs (n >= 0; dtypes as below;
+ * about 2n times the two element sizes).                                 */
+attn_status_t attn_wasserstein_scratch_size(int64_t n, int32_t a_dtype, int32_t b_dtype,
+                                            size_t* bytes);
+
+/*   a, b    : n device elements each, of a_dtype / b_dtype, any of
+ *             ATTN_F32, ATTN_BF16, ATTN_F64 (a and b may differ);
+ *             read only.  0 <= n <= 2^31 - 1.
+ *   scratch : device memory of at least the size above (the sorted keys
+ *             of both inputs and the partial sums; caller-owned).
+ *   out_host: host pointer, filled after the stream has synchronised (this
+ *             call synchronises its stream).  n == 0 gives NaN distances
+ *             without a launch.                                          */
+attn_status_t attn_wasserstein(const void* a, int32_t a_dtype, const void* b, int32_t b_dtype,
+                               int64_t n, void* scratch, size_t scratch_bytes,
+                               attn_wasserstein_t* out_host, void* stream);
 
 /* delta = rowsum(dO o O): for every row i of every (batch, head),
  * delta_i = sum_c dO[i,c] * O[i,c] -- the per-row term the attention backward

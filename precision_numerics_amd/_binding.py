@@ -17,7 +17,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libpnattn.so")
 
 ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE, ATTN_ERR_HIP = range(5)
-ATTN_F32, ATTN_BF16, ATTN_INT8 = 0, 1, 2
+ATTN_F32, ATTN_BF16, ATTN_INT8, ATTN_F64 = 0, 1, 2, 3
 
 
 class AttnProblem(ctypes.Structure):
@@ -52,6 +52,19 @@ class AttnDeviation(ctypes.Structure):
         return {name: getattr(self, name) for name, _ in self._fields_}
 
 
+class AttnWasserstein(ctypes.Structure):
+    _fields_ = [
+        ("w1", ctypes.c_double),
+        ("w2", ctypes.c_double),
+        ("winf", ctypes.c_double),
+        ("n", ctypes.c_int64),
+        ("n_nonfinite", ctypes.c_int64),
+    ]
+
+    def as_dict(self) -> dict:
+        return {name: getattr(self, name) for name, _ in self._fields_}
+
+
 class AttnError(RuntimeError):
     def __init__(self, status: int, message: str):
         super().__init__(f"{message} (status {status})")
@@ -70,6 +83,10 @@ _SIGNATURES = {
                        ctypes.POINTER(AttnDeviation), _P],
     "attn_quantize_int8": [_P, ctypes.c_int64, ctypes.c_int64, _P, _P, _P],
     "attn_bwd_delta": [ctypes.POINTER(AttnProblem), _P, _P, _P, _P],
+    "attn_wasserstein_scratch_size": [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                      ctypes.POINTER(ctypes.c_size_t)],
+    "attn_wasserstein": [_P, ctypes.c_int32, _P, ctypes.c_int32, ctypes.c_int64, _P,
+                         ctypes.c_size_t, ctypes.POINTER(AttnWasserstein), _P],
     "attn_status_string": [ctypes.c_int],
     "attn_last_error": [],
     "attn_version": [],
@@ -120,6 +137,8 @@ def _dtype_code(t) -> int:
     import torch
     if t.dtype == torch.float32:
         return ATTN_F32
+    if t.dtype == torch.float64:
+        return ATTN_F64
     if t.dtype == torch.bfloat16:
         return ATTN_BF16
     if t.dtype == torch.int8:
@@ -256,6 +275,32 @@ def attn_bwd_delta(o, d_o, *, delta=None, stream=None):
     _check(load().attn_bwd_delta(ctypes.byref(prob), _ptr(o), _ptr(d_o), _ptr(delta),
                                  _stream(stream)))
     return delta
+
+
+def attn_wasserstein_scratch_size(n: int, a_dtype: int, b_dtype: int) -> int:
+    b = ctypes.c_size_t(0)
+    _check(load().attn_wasserstein_scratch_size(int(n), int(a_dtype), int(b_dtype),
+                                                ctypes.byref(b)))
+    return b.value
+
+
+def attn_wasserstein(a, b, *, scratch=None, stream=None) -> dict:
+    """W1, W2 and W_inf between the value distributions of a and b (same
+    number of elements; fp32, bf16 or fp64 each), on the GPU."""
+    import torch
+    _contig(a, b, scratch)
+    n = a.numel()
+    if b.numel() != n:
+        raise ValueError("a and b differ in size")
+    ta, tb = _dtype_code(a), _dtype_code(b)
+    need = attn_wasserstein_scratch_size(n, ta, tb)
+    if scratch is None:
+        scratch = torch.empty(max(need, 1), dtype=torch.uint8, device=a.device)
+    res = AttnWasserstein()
+    _check(load().attn_wasserstein(_ptr(a), ta, _ptr(b), tb, n, _ptr(scratch),
+                                   scratch.numel() * scratch.element_size(), ctypes.byref(res),
+                                   _stream(stream)))
+    return res.as_dict()
 
 
 def attn_version() -> str:

@@ -126,7 +126,7 @@ const char* attn_status_string(attn_status_t s) {
 
 const char* attn_last_error(void) { return g_last_error.c_str(); }
 
-const char* attn_version(void) { return "pnattn 0.2.0 (gfx950)"; }
+const char* attn_version(void) { return "pnattn 0.3.0 (gfx950)"; }
 
 attn_status_t attn_bwd_delta(const attn_problem_t* prob, const void* o, const void* d_o,
                              float* delta, void* stream) {
@@ -261,6 +261,53 @@ attn_status_t attn_deviation(const void* o_test, int32_t o_dtype, const double* 
     out.rms = std::sqrt(r.sum_sq / (double)fin);
     out.rel_normwise = r.max_ref_abs > 0 ? r.max_abs / r.max_ref_abs
                                          : (r.max_abs == 0 ? 0.0 : INFINITY);
+  }
+  *out_host = out;
+  return ok();
+}
+
+static bool w_dtype_ok(int32_t t) { return t == ATTN_F32 || t == ATTN_BF16 || t == ATTN_F64; }
+
+attn_status_t attn_wasserstein_scratch_size(int64_t n, int32_t a_dtype, int32_t b_dtype,
+                                            size_t* bytes) {
+  if (bytes == nullptr) return fail(ATTN_ERR_INVALID_ARG, "bytes is NULL");
+  if (n < 0 || n > INT32_MAX) return fail(ATTN_ERR_INVALID_ARG, "n must be in [0, 2^31 - 1]");
+  if (!w_dtype_ok(a_dtype) || !w_dtype_ok(b_dtype))
+    return fail(ATTN_ERR_INVALID_ARG, "dtypes must be ATTN_F32, ATTN_BF16 or ATTN_F64");
+  *bytes = n == 0 ? 0 : pn::wasserstein_scratch_bytes(n, a_dtype, b_dtype);
+  return ok();
+}
+
+attn_status_t attn_wasserstein(const void* a, int32_t a_dtype, const void* b, int32_t b_dtype,
+                               int64_t n, void* scratch, size_t scratch_bytes,
+                               attn_wasserstein_t* out_host, void* stream) {
+  if (out_host == nullptr) return fail(ATTN_ERR_INVALID_ARG, "out_host is NULL");
+  if (n < 0 || n > INT32_MAX) return fail(ATTN_ERR_INVALID_ARG, "n must be in [0, 2^31 - 1]");
+  if (!w_dtype_ok(a_dtype) || !w_dtype_ok(b_dtype))
+    return fail(ATTN_ERR_INVALID_ARG, "dtypes must be ATTN_F32, ATTN_BF16 or ATTN_F64");
+  const double nan = std::nan("");
+  if (n == 0) {
+    *out_host = attn_wasserstein_t{nan, nan, nan, 0, 0};
+    return ok();
+  }
+  if (a == nullptr || b == nullptr || scratch == nullptr)
+    return fail(ATTN_ERR_INVALID_ARG, "a, b and scratch must be non-NULL");
+  const size_t need = pn::wasserstein_scratch_bytes(n, a_dtype, b_dtype);
+  if (scratch_bytes < need)
+    return fail(ATTN_ERR_WORKSPACE, "scratch has %zu bytes, needs %zu", scratch_bytes, need);
+  pn::WassersteinRecord r;
+  hipError_t e = pn::launch_wasserstein(a, a_dtype, b, b_dtype, n, scratch, &r,
+                                        (hipStream_t)stream);
+  if (e != hipSuccess) return from_hip(e, "attn_wasserstein");
+  attn_wasserstein_t out;
+  out.n = n;
+  out.n_nonfinite = r.n_nonfinite;
+  if (r.n_nonfinite > 0) {
+    out.w1 = out.w2 = out.winf = nan;
+  } else {
+    out.w1 = r.sum_abs / (double)n;
+    out.w2 = std::sqrt(r.sum_sq / (double)n);
+    out.winf = r.max_abs;
   }
   *out_host = out;
   return ok();

@@ -7,7 +7,7 @@
 
 namespace pn {
 
-enum DType : int { kF32 = 0, kBF16 = 1, kINT8 = 2 };
+enum DType : int { kF32 = 0, kBF16 = 1, kINT8 = 2, kF64 = 3 };
 
 struct AttnArgs {
   const void* q = nullptr;
@@ -45,6 +45,16 @@ struct DeviationRecord {
 hipError_t launch_deviation(const void* o_test, int o_dtype,
                             const double* o_ref, int64_t n, void* scratch,
                             DeviationRecord* out_host, hipStream_t stream);
+
+// Wasserstein distances of two n-element tensors (kF32, kBF16 or kF64):
+// sorted keys and partials live in scratch; the record holds the sums.
+struct WassersteinRecord {
+  double sum_abs, sum_sq, max_abs;
+  int64_t n_nonfinite;
+};
+size_t wasserstein_scratch_bytes(int64_t n, int a_dtype, int b_dtype);
+hipError_t launch_wasserstein(const void* a, int a_dtype, const void* b, int b_dtype, int64_t n,
+                              void* scratch, WassersteinRecord* out_host, hipStream_t stream);
 
 // delta = rowsum(dO o O) over rows of head_dim elements of the output dtype
 // (kF32, or bf16 for the others).

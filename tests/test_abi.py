@@ -156,3 +156,31 @@ def test_status_strings(clib):
 def test_missing_library_fails_loudly(tmp_path):
     with pytest.raises(RuntimeError, match="not built"):
         B.load(str(tmp_path / "libpnattn.so"))
+
+
+def test_wasserstein_validation(clib):
+    out = B.AttnWasserstein()
+    n = ctypes.c_size_t(0)
+    W = clib.attn_wasserstein
+    assert W(FAKE, B.ATTN_BF16, FAKE, B.ATTN_F64, 10, FAKE, 1 << 30, None, None) == 1
+    assert W(FAKE, B.ATTN_INT8, FAKE, B.ATTN_F64, 10, FAKE, 1 << 30, ctypes.byref(out), None) == 1
+    assert W(FAKE, B.ATTN_BF16, FAKE, 7, 10, FAKE, 1 << 30, ctypes.byref(out), None) == 1
+    assert W(FAKE, B.ATTN_BF16, FAKE, B.ATTN_F64, -1, FAKE, 1 << 30, ctypes.byref(out), None) == 1
+    assert W(FAKE, B.ATTN_BF16, FAKE, B.ATTN_F64, 1 << 31, FAKE, 1 << 40, ctypes.byref(out),
+             None) == 1
+    assert W(None, B.ATTN_BF16, FAKE, B.ATTN_F64, 10, FAKE, 1 << 30, ctypes.byref(out), None) == 1
+    assert W(FAKE, B.ATTN_BF16, FAKE, B.ATTN_F64, 10, FAKE, 16, ctypes.byref(out), None) == 3
+    assert W(None, B.ATTN_BF16, None, B.ATTN_F64, 0, None, 0, ctypes.byref(out), None) == 0
+    assert out.n == 0 and out.w1 != out.w1          # NaN: no distribution
+    assert clib.attn_wasserstein_scratch_size(100, B.ATTN_BF16, B.ATTN_F64, ctypes.byref(n)) == 0
+    assert n.value >= 100 * 2 * (2 + 8)
+    assert clib.attn_wasserstein_scratch_size(100, B.ATTN_INT8, B.ATTN_F64, ctypes.byref(n)) == 1
+
+
+def test_f64_is_not_an_attention_dtype(clib):
+    p = _prob(dtype=B.ATTN_F64)
+    assert clib.attn_fwd_flash(ctypes.byref(p), FAKE, FAKE, FAKE, None, None, FAKE, None,
+                               None) == B.ATTN_ERR_INVALID_ARG
+    out = B.AttnDeviation()
+    assert clib.attn_deviation(FAKE, B.ATTN_F64, FAKE, 10, FAKE, 1 << 20, ctypes.byref(out),
+                               None) == B.ATTN_ERR_INVALID_ARG
