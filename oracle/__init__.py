@@ -9,8 +9,11 @@ from .attention import (default_scale, attention, attention_head, int8_scores,
                         deviation, attention_probabilities, attention_delta,
                         run_heads)
 from .distance import wasserstein, wasserstein1_cdf
+from .fp8 import (E4M3_MAX, e4m3_decode, e4m3_encode, quantize_fp8, fp8_scores,
+                  attention_fp8_head, attention_fp8)
 
 __all__ = ["default_scale", "attention", "attention_head", "int8_scores",
            "attention_int8", "attention_int8_head", "quantize_int8",
            "deviation", "attention_probabilities", "attention_delta", "run_heads",
-           "wasserstein", "wasserstein1_cdf"]
+           "wasserstein", "wasserstein1_cdf", "E4M3_MAX", "e4m3_decode", "e4m3_encode",
+           "quantize_fp8", "fp8_scores", "attention_fp8_head", "attention_fp8"]

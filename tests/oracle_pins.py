@@ -462,3 +462,100 @@ def check_wasserstein(ora):
     # non-finite inputs
     w = ora.wasserstein([1.0, float("nan"), float("inf")], [0.0, 1.0, 2.0])
     assert w["n_nonfinite"] == 2 and math.isnan(w["w1"]) and math.isnan(w["winf"])
+
+
+# ---------------------------------------------------------------------------
+# E4M3 fp8 Q/K path
+# ---------------------------------------------------------------------------
+
+def _torch_e4m3():
+    import torch
+    return torch, torch.float8_e4m3fn
+
+
+@pin
+def check_e4m3_codec(ora):
+    """Decode and encode against torch's float8_e4m3fn (all 256 patterns;
+    round to nearest even inside the range), closed forms for ties,
+    saturation, signed zero and NaN, and the round trip of every code."""
+    torch, f8 = _torch_e4m3()
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(f8).float().double().numpy()
+    got = ora.e4m3_decode(codes)
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    fin = ~np.isnan(ref)
+    assert np.array_equal(got[fin], ref[fin])
+    assert np.array_equal(np.signbit(got[fin]), np.signbit(ref[fin]))
+    rng = _rng(61)
+    x = np.concatenate([rng.standard_normal(20000) * 40.0,
+                        rng.standard_normal(5000) * 2.0 ** -8,           # subnormal range
+                        ora.e4m3_decode(rng.integers(0, 0x7f, 3000)) * (1 + 2.0 ** -4),
+                        (ora.e4m3_decode(np.arange(1, 0x7e)) +
+                         ora.e4m3_decode(np.arange(2, 0x7f))) / 2]).astype(np.float32)
+    x = x[np.abs(x) < 464]
+    tq = torch.from_numpy(x).to(f8).view(torch.uint8).numpy()
+    assert np.array_equal(ora.e4m3_encode(x), tq)
+    fin_codes = np.array([c for c in range(256) if (c & 0x7f) != 0x7f], dtype=np.uint8)
+    assert np.array_equal(ora.e4m3_encode(ora.e4m3_decode(fin_codes)), fin_codes)
+    assert ora.e4m3_decode([0x38])[0] == 1.0 and ora.e4m3_decode([0x7e])[0] == 448.0
+    assert ora.e4m3_decode([0x01])[0] == 2.0 ** -9 and ora.e4m3_decode([0x08])[0] == 2.0 ** -6
+    enc = ora.e4m3_encode(np.array([1.0625, 1.1875, 449.0, 1e4, -1e4, -0.0, 2.0 ** -10,
+                                    3 * 2.0 ** -10, np.nan]))
+    assert list(enc) == [0x38, 0x3A, 0x7E, 0x7E, 0xFE, 0x80, 0x00, 0x02, 0x7F], list(enc)
+
+
+@pin
+def check_fp8_quantiser(ora):
+    """Per-row E4M3 quantiser: the row maximum maps to +-448, every code is
+    finite, the dequantised value is within half a spacing (1/16 relative,
+    or 2^-10 * scale in the subnormal range) of x, and an all-zero row gets
+    scale 1 and zero codes."""
+    rng = _rng(67)
+    x = (rng.standard_normal((40, 96)) * np.exp(rng.standard_normal((40, 1)) * 3)).astype(np.float32)
+    x[3] = 0.0
+    codes, scale = ora.quantize_fp8(x)
+    assert codes.dtype == np.uint8 and scale.dtype == np.float32 and scale.shape == (40,)
+    assert np.all((codes & 0x7F) != 0x7F)
+    assert scale[3] == 1.0 and not codes[3].any()
+    vals = ora.e4m3_decode(codes)
+    for r in range(40):
+        if r == 3:
+            continue
+        i = int(np.argmax(np.abs(x[r])))
+        assert abs(vals[r, i]) == 448.0
+        assert np.array_equal(np.signbit(vals[r]), np.signbit(x[r]))
+        err = np.abs(vals[r] * np.float64(scale[r]) - x[r].astype(np.float64))
+        bound = np.maximum(np.abs(x[r]) / 16.0, 2.0 ** -10 * scale[r]) * (1 + 1e-6)
+        assert np.all(err <= bound)
+    assert np.float32(np.abs(x[0]).max() / np.float32(448.0)) == scale[0]
+
+
+@pin
+def check_fp8_scores_and_attention(ora):
+    """Dot products of decoded codes equal exact integer arithmetic (every
+    value is an integer multiple of 2^-9), and fp8 attention equals the
+    plain oracle on the dequantised Q and K."""
+    rng = _rng(71)
+    qc = rng.integers(0, 256, (6, 16)).astype(np.uint8)
+    kc = rng.integers(0, 256, (5, 16)).astype(np.uint8)
+    qc[(qc & 0x7F) == 0x7F] = 0x3C
+    kc[(kc & 0x7F) == 0x7F] = 0xB1
+    got = ora.fp8_scores(qc, kc)
+    qi = [[int(round(float(v) * 512)) for v in row] for row in ora.e4m3_decode(qc)]
+    ki = [[int(round(float(v) * 512)) for v in row] for row in ora.e4m3_decode(kc)]
+    for i in range(6):
+        for j in range(5):
+            exact = sum(a * b for a, b in zip(qi[i], ki[j]))
+            assert got[i, j] == exact / 2.0 ** 18
+    q = rng.standard_normal((2, 3, 40, 32)).astype(np.float32)
+    k = rng.standard_normal((2, 3, 40, 32)).astype(np.float32) * 3
+    v = rng.standard_normal((2, 3, 40, 32))
+    qq, qs = ora.quantize_fp8(q)
+    kq, ks = ora.quantize_fp8(k)
+    for causal in (False, True):
+        o, lse = ora.attention_fp8(qq, qs, kq, ks, v, causal=causal, scale=0.3)
+        qd = ora.e4m3_decode(qq) * qs[..., None].astype(np.float64)
+        kd = ora.e4m3_decode(kq) * ks[..., None].astype(np.float64)
+        o2, lse2 = ora.attention(qd, kd, v, causal=causal, scale=0.3)
+        assert np.allclose(o, o2, rtol=1e-12, atol=1e-13)
+        assert np.allclose(lse, lse2, rtol=1e-12, atol=1e-13)

@@ -12,6 +12,7 @@ import oracle_pins
 ORACLE_DIR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle")
 SRC = os.path.join(ORACLE_DIR, "attention.py")
 DIST_SRC = os.path.join(ORACLE_DIR, "distance.py")
+FP8_SRC = os.path.join(ORACLE_DIR, "fp8.py")
 
 MUTANTS = [
     ("diagonal dropped from causal mask", "return cols <= rows", "return cols < rows"),
@@ -90,20 +91,46 @@ DIST_MUTANTS = [
 ]
 
 
+FP8_MUTANTS = [
+    ("E4M3 exponent bias 8", "return sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)",
+     "return sign * (1.0 + m / 8.0) * 2.0 ** (e - 8)"),
+    ("E4M3 subnormals one binade low", "return sign * (m / 8.0) * 2.0 ** -6",
+     "return sign * (m / 8.0) * 2.0 ** -7"),
+    ("E4M3 ties away from zero", "pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))",
+     "pick_hi = (d_hi <= d_lo)"),
+    ("E4M3 ties to odd", "pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))",
+     "pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 1))"),
+    ("E4M3 sign of -0 lost", "np.where(np.signbit(x), 0x80, 0)", "np.where(x < 0, 0x80, 0)"),
+    ("E4M3 NaN not mapped", "code = np.where(np.isnan(x), 0x7F, code)", "code = code"),
+    ("fp8 quantiser divides by 447", "scale = (absmax / np.float32(E4M3_MAX))",
+     "scale = (absmax / np.float32(447.0))"),
+    ("fp8 quantiser zero-row guard dropped",
+     "scale = np.where(scale == np.float32(0.0), np.float32(1.0), scale)",
+     "scale = np.where(scale == np.float32(0.0), np.float32(0.0), scale)"),
+    ("fp8 key scale dropped", "return scale * sq[r0:r1, None] * sk[None, :kend] * dots",
+     "return scale * sq[r0:r1, None] * dots"),
+    ("fp8 scores transposed", "return qd @ np.swapaxes(kd, -1, -2)",
+     "return kd @ np.swapaxes(qd, -1, -2)"),
+]
+
+
 def _mutant_module(old, new, path=SRC):
-    """The oracle's two modules in one namespace, one of them mutated."""
+    """The oracle's modules in one namespace (their relative imports then
+    resolve there), one of them mutated."""
     mod = types.ModuleType("oracle_mutant")
-    for src_path in (SRC, DIST_SRC):
+    for src_path in (SRC, DIST_SRC, FP8_SRC):
         src = open(src_path).read()
         if src_path == path:
             assert src.count(old) == 1, f"mutation site not unique: {old!r}"
             src = src.replace(old, new)
+        src = "\n".join(line for line in src.split("\n") if not line.startswith("from ."))
         exec(compile(src, src_path + " (mutant)", "exec"), mod.__dict__)
     return mod
 
 
 ALL_MUTANTS = [(n, o, w, SRC) for n, o, w in MUTANTS] + \
-              [(n, o, w, DIST_SRC) for n, o, w in DIST_MUTANTS]
+              [(n, o, w, DIST_SRC) for n, o, w in DIST_MUTANTS] + \
+              [(n, o, w, FP8_SRC) for n, o, w in FP8_MUTANTS]
 
 
 @pytest.mark.parametrize("name,old,new,path", ALL_MUTANTS, ids=[m[0] for m in ALL_MUTANTS])
@@ -123,5 +150,8 @@ def test_unmutated_copy_passes_all_pins():
     for check in oracle_pins.PINS:
         check(mod)
     mod = _mutant_module("def wasserstein(", "def wasserstein(", DIST_SRC)
+    for check in oracle_pins.PINS:
+        check(mod)
+    mod = _mutant_module("def e4m3_encode(", "def e4m3_encode(", FP8_SRC)
     for check in oracle_pins.PINS:
         check(mod)
