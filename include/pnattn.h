@@ -17,7 +17,7 @@
  *
  * Conventions shared by all entry points
  *  - Layout: contiguous [batch][heads][seq_len][head_dim] ("BHSD"), head_dim
- *    fastest; int8 scales are [batch][heads][seq_len].
+ *    fastest; int8 and fp8 scales are [batch][heads][seq_len].
  *  - Pointers are device pointers (hipMalloc'd or torch CUDA tensors) unless
  *    named *_host.  The caller owns every buffer; the library allocates no
  *    device memory and keeps no state besides a thread-local error string.
@@ -52,7 +52,14 @@ typedef enum {
   ATTN_BF16 = 1, /* Q, K, V and O are bf16                                 */
   ATTN_INT8 = 2, /* Q, K are int8 codes with fp32 per-row scales;
                     V and O are bf16                                        */
-  ATTN_F64 = 3   /* fp64 values: only as an input of attn_wasserstein      */
+  ATTN_F64 = 3,  /* fp64 values: only as an input of attn_wasserstein      */
+  ATTN_FP8 = 4   /* Q, K are E4M3 fp8 codes ("FP8 Formats for Deep
+                    Learning": sign, 4 exponent bits of bias 7, 3 mantissa
+                    bits, max 448) with fp32 per-row scales; V and O are
+                    bf16.  S = scale * sq_i * sk_j * (Qd Kd^T)_ij of the
+                    decoded codes; the fp8 matrix products sum their terms
+                    with less than fp32 precision (about 7e-5 of the
+                    largest partial sum)                                   */
 } attn_dtype_t;
 
 typedef struct {
@@ -97,9 +104,11 @@ typedef struct {
  * as that page's Figure 5 caption notes: to within an ulp in fp32, exactly
  * once rounded to bf16), and an exp-rescaled fp32 output accumulator;
  * O = acc / l at the end.  S is never stored.
- *   q, k   : [B,H,N,d] of dtype (int8 codes for ATTN_INT8)
+ *   q, k   : [B,H,N,d] of dtype (int8 codes for ATTN_INT8, E4M3 bytes
+ *            for ATTN_FP8)
  *   v, o   : [B,H,N,d] fp32 for ATTN_F32, bf16 otherwise
- *   q_scale, k_scale : [B,H,N] fp32, required for ATTN_INT8, else NULL
+ *   q_scale, k_scale : [B,H,N] fp32, required for ATTN_INT8 and ATTN_FP8,
+ *            else NULL
  *   lse    : optional [B,H,N] fp32 log-sum-exp of each score row (natural
  *            log, scaled scores), or NULL.                                 */
 attn_status_t attn_fwd_flash(const attn_problem_t* prob, const void* q,
@@ -119,7 +128,8 @@ attn_status_t attn_fwd_flash_debug_s(const attn_problem_t* prob, const void* q,
                                      int32_t* s_out, void* stream);
 
 /* Bytes of workspace attn_fwd_baseline needs: S [B,H,N,N] (fp32, or int32
- * for ATTN_INT8) followed by P [B,H,N,N] (bf16 if p_bf16, else fp32).    */
+ * for ATTN_INT8) followed by P [B,H,N,N] (bf16 if p_bf16, else fp32).  For
+ * ATTN_INT8 and ATTN_FP8, S holds the unscaled code products.            */
 attn_status_t attn_baseline_workspace_size(const attn_problem_t* prob,
                                            size_t* bytes);
 
@@ -218,6 +228,16 @@ attn_status_t attn_bwd_delta(const attn_problem_t* prob, const void* o,
  * codes: [rows][d] int8, scales: [rows] fp32.  1 <= d <= 1024.            */
 attn_status_t attn_quantize_int8(const float* x, int64_t rows, int64_t d,
                                  int8_t* codes, float* scales, void* stream);
+
+/* The same per-row scheme with E4M3 fp8 codes (ATTN_FP8; the per-row
+ * absmax/448 scale is this library's reading, as for int8):
+ *   scale_r = fp32(absmax_r / 448)  (IEEE division), 1 if that is 0;
+ *   code    = E4M3(fp32(x / scale_r)): nearest, ties to the even code,
+ *             magnitudes at or above 448 give 448, the sign bit is x's
+ *             (a NaN input gives 0x7f).
+ * codes: [rows][d] uint8, scales: [rows] fp32.  1 <= d <= 1024.           */
+attn_status_t attn_quantize_fp8(const float* x, int64_t rows, int64_t d,
+                                uint8_t* codes, float* scales, void* stream);
 
 const char* attn_status_string(attn_status_t status);
 /* Detail of the last failing call on this thread ("" if none).           */

@@ -17,7 +17,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libpnattn.so")
 
 ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE, ATTN_ERR_HIP = range(5)
-ATTN_F32, ATTN_BF16, ATTN_INT8, ATTN_F64 = 0, 1, 2, 3
+ATTN_F32, ATTN_BF16, ATTN_INT8, ATTN_F64, ATTN_FP8 = 0, 1, 2, 3, 4
 
 
 class AttnProblem(ctypes.Structure):
@@ -82,6 +82,7 @@ _SIGNATURES = {
     "attn_deviation": [_P, ctypes.c_int32, _P, ctypes.c_int64, _P, ctypes.c_size_t,
                        ctypes.POINTER(AttnDeviation), _P],
     "attn_quantize_int8": [_P, ctypes.c_int64, ctypes.c_int64, _P, _P, _P],
+    "attn_quantize_fp8": [_P, ctypes.c_int64, ctypes.c_int64, _P, _P, _P],
     "attn_bwd_delta": [ctypes.POINTER(AttnProblem), _P, _P, _P, _P],
     "attn_wasserstein_scratch_size": [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                       ctypes.POINTER(ctypes.c_size_t)],
@@ -143,6 +144,8 @@ def _dtype_code(t) -> int:
         return ATTN_BF16
     if t.dtype == torch.int8:
         return ATTN_INT8
+    if t.dtype == torch.uint8:
+        return ATTN_FP8
     raise TypeError(f"unsupported q/k dtype {t.dtype}")
 
 
@@ -164,7 +167,7 @@ def make_problem(q, *, causal: bool, p_bf16: bool = True, softmax_scale: float =
 
 def _out_like(q, v):
     import torch
-    if q.dtype == torch.int8:
+    if q.dtype in (torch.int8, torch.uint8):
         return torch.empty(q.shape[:-1] + (v.shape[-1],), dtype=v.dtype, device=v.device)
     return torch.empty_like(v)
 
@@ -258,6 +261,23 @@ def attn_quantize_int8(x, *, codes=None, scales=None, stream=None):
               if scales is None else scales)
     _check(load().attn_quantize_int8(_ptr(x), rows, d, _ptr(codes), _ptr(scales),
                                      _stream(stream)))
+    return codes, scales
+
+
+def attn_quantize_fp8(x, *, codes=None, scales=None, stream=None):
+    """Per-row E4M3 fp8 quantisation of fp32 x[..., d]; returns (codes as
+    uint8 bytes, scales)."""
+    import torch
+    _contig(x, codes, scales)
+    if x.dtype != torch.float32:
+        raise TypeError("x must be float32")
+    d = x.shape[-1]
+    rows = x.numel() // d if d else 0
+    codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device) if codes is None else codes
+    scales = (torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
+              if scales is None else scales)
+    _check(load().attn_quantize_fp8(_ptr(x), rows, d, _ptr(codes), _ptr(scales),
+                                    _stream(stream)))
     return codes, scales
 
 

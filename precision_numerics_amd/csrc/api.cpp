@@ -65,7 +65,8 @@ attn_status_t check_problem(const attn_problem_t* prob, const void* q, const voi
     return fail(ATTN_ERR_INVALID_ARG, "causal must be 0 or 1 (got %d)", prob->causal);
   if (prob->p_bf16 != 0 && prob->p_bf16 != 1)
     return fail(ATTN_ERR_INVALID_ARG, "p_bf16 must be 0 or 1 (got %d)", prob->p_bf16);
-  if (prob->dtype != ATTN_F32 && prob->dtype != ATTN_BF16 && prob->dtype != ATTN_INT8)
+  if (prob->dtype != ATTN_F32 && prob->dtype != ATTN_BF16 && prob->dtype != ATTN_INT8 &&
+      prob->dtype != ATTN_FP8)
     return fail(ATTN_ERR_INVALID_ARG, "unknown dtype %d", prob->dtype);
   if (!std::isfinite(prob->softmax_scale))
     return fail(ATTN_ERR_INVALID_ARG, "softmax_scale is not finite");
@@ -80,11 +81,11 @@ attn_status_t check_problem(const attn_problem_t* prob, const void* q, const voi
     if (prob->dtype != ATTN_BF16)
       return fail(ATTN_ERR_UNSUPPORTED, "the stabilized variant is built for ATTN_BF16 only");
   }
-  const bool i8 = prob->dtype == ATTN_INT8;
-  if (i8 && (q_scale == nullptr || k_scale == nullptr))
-    return fail(ATTN_ERR_INVALID_ARG, "ATTN_INT8 needs q_scale and k_scale");
-  if (!i8 && (q_scale != nullptr || k_scale != nullptr))
-    return fail(ATTN_ERR_INVALID_ARG, "q_scale/k_scale are only for ATTN_INT8");
+  const bool scaled = prob->dtype == ATTN_INT8 || prob->dtype == ATTN_FP8;
+  if (scaled && (q_scale == nullptr || k_scale == nullptr))
+    return fail(ATTN_ERR_INVALID_ARG, "ATTN_INT8 and ATTN_FP8 need q_scale and k_scale");
+  if (!scaled && (q_scale != nullptr || k_scale != nullptr))
+    return fail(ATTN_ERR_INVALID_ARG, "q_scale/k_scale are only for ATTN_INT8 and ATTN_FP8");
   *empty = prob->batch == 0 || prob->heads == 0 || prob->seq_len == 0;
   if (!*empty && (q == nullptr || k == nullptr || v == nullptr || o == nullptr))
     return fail(ATTN_ERR_INVALID_ARG, "q, k, v and o must be non-NULL");
@@ -139,7 +140,8 @@ attn_status_t attn_bwd_delta(const attn_problem_t* prob, const void* o, const vo
   if (prob->head_dim != 64 && prob->head_dim != 128)
     return fail(ATTN_ERR_UNSUPPORTED, "head_dim %lld not built (64 or 128)",
                 (long long)prob->head_dim);
-  if (prob->dtype != ATTN_F32 && prob->dtype != ATTN_BF16 && prob->dtype != ATTN_INT8)
+  if (prob->dtype != ATTN_F32 && prob->dtype != ATTN_BF16 && prob->dtype != ATTN_INT8 &&
+      prob->dtype != ATTN_FP8)
     return fail(ATTN_ERR_INVALID_ARG, "unknown dtype %d", prob->dtype);
   if (prob->batch > 0 && prob->heads > INT64_MAX / prob->batch)
     return fail(ATTN_ERR_UNSUPPORTED, "batch*heads too large");
@@ -311,6 +313,18 @@ attn_status_t attn_wasserstein(const void* a, int32_t a_dtype, const void* b, in
   }
   *out_host = out;
   return ok();
+}
+
+attn_status_t attn_quantize_fp8(const float* x, int64_t rows, int64_t d, uint8_t* codes,
+                                float* scales, void* stream) {
+  if (rows < 0) return fail(ATTN_ERR_INVALID_ARG, "rows must be >= 0");
+  if (d < 1 || d > 1024) return fail(ATTN_ERR_INVALID_ARG, "d must be in [1, 1024] (got %lld)", (long long)d);
+  if (rows == 0) return ok();
+  if (x == nullptr || codes == nullptr || scales == nullptr)
+    return fail(ATTN_ERR_INVALID_ARG, "x, codes and scales must be non-NULL");
+  if ((rows + 3) / 4 > INT32_MAX) return fail(ATTN_ERR_UNSUPPORTED, "too many rows");
+  return from_hip(pn::launch_quantize_fp8(x, rows, d, codes, scales, (hipStream_t)stream),
+                  "attn_quantize_fp8 launch");
 }
 
 attn_status_t attn_quantize_int8(const float* x, int64_t rows, int64_t d, int8_t* codes,

@@ -4,7 +4,8 @@
 // plain, non-fused attention ("Baseline Attention") in an isolated forward
 // pass.  Three kernels on one stream, each a separate pass over HBM:
 //   K1 scores : S = scale * Q K^T for all N x N (query, key) pairs, fp32
-//               (int8 Q/K: the exact int32 products Qc Kc^T, unscaled)
+//               (int8 Q/K: the exact int32 products Qc Kc^T, unscaled;
+//               E4M3 fp8 Q/K: the fp32 products of the codes, unscaled)
 //   K2 softmax: per row, the causal mask, the row max, exp, the row sum and
 //               the normalised P = e / sum in fp32, stored as bf16 (RNE) or
 //               fp32
@@ -28,7 +29,7 @@ constexpr int kThreads = 256;
 // rows and all 128 keys (4 MFMA tiles).  Operands come straight from global
 // memory (16-byte loads along d), the output leaves in 128-byte row segments.
 // ---------------------------------------------------------------------------
-template <int D, int QK>  // QK: 0 bf16, 1 int8, 2 fp32
+template <int D, int QK>  // QK: 0 bf16, 1 int8, 2 fp32, 3 E4M3 fp8
 __global__ __launch_bounds__(kThreads) void scores_kernel(const void* qp, const void* kp,
                                                          void* sp, int N, float scale) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -38,7 +39,7 @@ __global__ __launch_bounds__(kThreads) void scores_kernel(const void* qp, const 
   const int j0 = blockIdx.x * 128;
   const int64_t hoff = bh * (int64_t)N * D;
   const int qi = i0 + n;  // A-operand row of this lane
-  if constexpr (QK == 0 || QK == 1) {
+  if constexpr (QK == 0 || QK == 1 || QK == 3) {
     using T = typename std::conditional<QK == 0, uint16_t, int8_t>::type;
     constexpr int EPC = 16 / (int)sizeof(T);
     constexpr int ST = D / (2 * EPC);
@@ -52,7 +53,7 @@ __global__ __launch_bounds__(kThreads) void scores_kernel(const void* qp, const 
 #pragma unroll
     for (int jt = 0; jt < 4; ++jt) {
       const int kj = j0 + 32 * jt + n;  // B-operand column of this lane
-      using Acc = typename std::conditional<QK == 0, f32x16, i32x16>::type;
+      using Acc = typename std::conditional<QK == 1, i32x16, f32x16>::type;
       Acc acc = {};
 #pragma unroll
       for (int t = 0; t < ST; ++t) {
@@ -60,8 +61,10 @@ __global__ __launch_bounds__(kThreads) void scores_kernel(const void* qp, const 
                                : i32x4{0, 0, 0, 0};
         if constexpr (QK == 0)
           acc = mfma_bf16(__builtin_bit_cast(bf16x8, a[t]), __builtin_bit_cast(bf16x8, b), acc);
-        else
+        else if constexpr (QK == 1)
           acc = mfma_i8(a[t], b, acc);
+        else
+          acc = mfma_fp8x2(a[t], b, acc);
       }
       if (kj < N) {
 #pragma unroll
@@ -71,8 +74,10 @@ __global__ __launch_bounds__(kThreads) void scores_kernel(const void* qp, const 
             const int64_t off = (bh * N + i) * (int64_t)N + kj;
             if constexpr (QK == 0)
               ((float*)sp)[off] = acc[r] * scale;
-            else
+            else if constexpr (QK == 1)
               ((int32_t*)sp)[off] = acc[r];
+            else
+              ((float*)sp)[off] = acc[r];  // unscaled; K2 applies the row scales
           }
         }
       }
@@ -120,7 +125,9 @@ __device__ __forceinline__ float block_reduce(float x, bool is_max, float* red) 
   return r;
 }
 
-template <bool INT8S, bool PBF16>
+// SMODE: 0 scores already scaled (fp32), 1 int32 products of int8 codes,
+// 2 fp32 products of E4M3 codes; 1 and 2 apply scale * sq_i * sk_j here.
+template <int SMODE, bool PBF16>
 __global__ __launch_bounds__(kThreads) void softmax_kernel(const void* sp, void* pp,
                                                           const float* q_scale,
                                                           const float* k_scale, int N,
@@ -130,10 +137,12 @@ __global__ __launch_bounds__(kThreads) void softmax_kernel(const void* sp, void*
   const int64_t bh = blockIdx.y;
   const int64_t row = (bh * N + i) * (int64_t)N;
   const int jend = causal ? i + 1 : N;  // visible keys: j < jend
-  const float sqc = INT8S ? q_scale[bh * N + i] * scale : 0.f;
+  const float sqc = SMODE != 0 ? q_scale[bh * N + i] * scale : 0.f;
   auto score = [&](int j) -> float {
-    if constexpr (INT8S)
+    if constexpr (SMODE == 1)
       return (float)((const int32_t*)sp)[row + j] * (k_scale[bh * N + j] * sqc);
+    else if constexpr (SMODE == 2)
+      return ((const float*)sp)[row + j] * (k_scale[bh * N + j] * sqc);
     else
       return ((const float*)sp)[row + j];
   };
@@ -271,6 +280,8 @@ hipError_t launch_scores(const AttnArgs& a, void* s, hipStream_t st) {
     hipLaunchKernelGGL((scores_kernel<D, 0>), grid, dim3(kThreads), 0, st, a.q, a.k, s, N, a.scale);
   else if (a.dtype == kINT8)
     hipLaunchKernelGGL((scores_kernel<D, 1>), grid, dim3(kThreads), 0, st, a.q, a.k, s, N, a.scale);
+  else if (a.dtype == kFP8)
+    hipLaunchKernelGGL((scores_kernel<D, 3>), grid, dim3(kThreads), 0, st, a.q, a.k, s, N, a.scale);
   else
     hipLaunchKernelGGL((scores_kernel<D, 2>), grid, dim3(kThreads), 0, st, a.q, a.k, s, N, a.scale);
   return hipGetLastError();
@@ -307,15 +318,19 @@ hipError_t launch_baseline(const AttnArgs& a, void* workspace, hipStream_t st) {
   hipError_t e = a.head_dim == 64 ? launch_scores<64>(a, s, st) : launch_scores<128>(a, s, st);
   if (e != hipSuccess) return e;
   dim3 grid2((unsigned)N, (unsigned)bh);
-  const bool i8 = a.dtype == kINT8;
-  if (i8 && a.p_bf16)
-    hipLaunchKernelGGL((softmax_kernel<true, true>), grid2, dim3(kThreads), 0, st, s, p, a.q_scale, a.k_scale, N, a.causal, a.scale);
-  else if (i8)
-    hipLaunchKernelGGL((softmax_kernel<true, false>), grid2, dim3(kThreads), 0, st, s, p, a.q_scale, a.k_scale, N, a.causal, a.scale);
+  const int mode = a.dtype == kINT8 ? 1 : (a.dtype == kFP8 ? 2 : 0);
+  if (mode == 1 && a.p_bf16)
+    hipLaunchKernelGGL((softmax_kernel<1, true>), grid2, dim3(kThreads), 0, st, s, p, a.q_scale, a.k_scale, N, a.causal, a.scale);
+  else if (mode == 1)
+    hipLaunchKernelGGL((softmax_kernel<1, false>), grid2, dim3(kThreads), 0, st, s, p, a.q_scale, a.k_scale, N, a.causal, a.scale);
+  else if (mode == 2 && a.p_bf16)
+    hipLaunchKernelGGL((softmax_kernel<2, true>), grid2, dim3(kThreads), 0, st, s, p, a.q_scale, a.k_scale, N, a.causal, a.scale);
+  else if (mode == 2)
+    hipLaunchKernelGGL((softmax_kernel<2, false>), grid2, dim3(kThreads), 0, st, s, p, a.q_scale, a.k_scale, N, a.causal, a.scale);
   else if (a.p_bf16)
-    hipLaunchKernelGGL((softmax_kernel<false, true>), grid2, dim3(kThreads), 0, st, s, p, a.q_scale, a.k_scale, N, a.causal, a.scale);
+    hipLaunchKernelGGL((softmax_kernel<0, true>), grid2, dim3(kThreads), 0, st, s, p, a.q_scale, a.k_scale, N, a.causal, a.scale);
   else
-    hipLaunchKernelGGL((softmax_kernel<false, false>), grid2, dim3(kThreads), 0, st, s, p, a.q_scale, a.k_scale, N, a.causal, a.scale);
+    hipLaunchKernelGGL((softmax_kernel<0, false>), grid2, dim3(kThreads), 0, st, s, p, a.q_scale, a.k_scale, N, a.causal, a.scale);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   return a.head_dim == 64 ? launch_pv<64>(a, p, st) : launch_pv<128>(a, p, st);

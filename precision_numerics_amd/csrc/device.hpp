@@ -83,5 +83,39 @@ __device__ __forceinline__ i32x16 mfma_i8(i32x4 a, i32x4 b, i32x16 c) {
 __device__ __forceinline__ f32x16 mfma_f32(float a, float b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
+// Two E4M3 (OCP fp8, bias 7 on gfx950) products of 32x32x16 over the 16
+// bytes of an int8-style operand chunk: the low eight bytes of every lane
+// form one 16-deep product and the high eight the other, a consistent
+// split of the 32 k-values of the chunk between the A and B operands.
+// The hardware sums each product's 16 terms with less than fp32 precision
+// (about 7e-5 of the largest partial sum, measured on random operands).
+__device__ __forceinline__ f32x16 mfma_fp8x2(i32x4 a, i32x4 b, f32x16 c) {
+  const long alo = (long)(((uint64_t)(uint32_t)a[1] << 32) | (uint32_t)a[0]);
+  const long ahi = (long)(((uint64_t)(uint32_t)a[3] << 32) | (uint32_t)a[2]);
+  const long blo = (long)(((uint64_t)(uint32_t)b[1] << 32) | (uint32_t)b[0]);
+  const long bhi = (long)(((uint64_t)(uint32_t)b[3] << 32) | (uint32_t)b[2]);
+  c = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(alo, blo, c, 0, 0, 0);
+  return __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(ahi, bhi, c, 0, 0, 0);
+}
+
+// fp32 -> E4M3 code, round to nearest with ties to even; magnitudes at or
+// above 448 saturate to 448, NaN gives 0x7f, the sign bit is the input's.
+__device__ __forceinline__ uint8_t f32_to_e4m3(float x) {
+  const uint32_t bits = __float_as_uint(x);
+  const uint32_t sign = (bits >> 24) & 0x80u;
+  const float a = fabsf(x);
+  if (a != a) return 0x7f;
+  if (a >= 448.0f) return (uint8_t)(sign | 0x7eu);
+  uint32_t mag;
+  if (a < 0.015625f) {  // below 2^-6: multiples of 2^-9 (code = multiple)
+    mag = (uint32_t)rintf(a * 512.0f);
+  } else {  // round the fp32 significand to 3 bits, ties to even
+    const uint32_t ab = __float_as_uint(a);
+    const uint32_t r = (ab + 0x7ffffu + ((ab >> 20) & 1u)) >> 20;  // exponent:mantissa
+    mag = r - ((127u - 7u) << 3);
+    if (mag > 0x7eu) mag = 0x7eu;
+  }
+  return (uint8_t)(sign | mag);
+}
 
 }  // namespace pn

@@ -51,7 +51,9 @@
 namespace pn {
 namespace {
 
-enum QKKind { QK_BF16 = 0, QK_I8 = 1, QK_F32 = 2 };
+enum QKKind { QK_BF16 = 0, QK_I8 = 1, QK_F32 = 2, QK_F8 = 3 };
+// 8-bit Q/K codes with per-row fp32 scales (int8, or E4M3 fp8)
+template <int QK> constexpr bool kScaledQK = QK == QK_I8 || QK == QK_F8;
 // P*V engines: bf16 P and bf16 V on bf16 MFMA; otherwise fp32 MFMA with V
 // widened exactly (V stored as bf16 or as fp32).
 enum PVKind { PV_BF16 = 0, PV_F32_VBF16 = 1, PV_F32_VF32 = 2 };
@@ -69,6 +71,7 @@ template <int QK> struct QKTraits;
 template <> struct QKTraits<QK_BF16> { using T = uint16_t; };
 template <> struct QKTraits<QK_I8> { using T = int8_t; };
 template <> struct QKTraits<QK_F32> { using T = float; };
+template <> struct QKTraits<QK_F8> { using T = uint8_t; };
 template <int PV> struct VTraits { using T = uint16_t; };
 template <> struct VTraits<PV_F32_VF32> { using T = float; };
 
@@ -92,7 +95,7 @@ template <int D, int QK, int PV> struct Tile {
   static constexpr int kSegKPerWave = (kSegK + kIssuers - 1) / kIssuers;
   static constexpr int kSegVPerWave = (kSegV + kIssuers - 1) / kIssuers;
   static constexpr int kSegPerWave = kSegKPerWave > kSegVPerWave ? kSegKPerWave : kSegVPerWave;
-  static constexpr int kBytesSk = (QK == QK_I8) ? kBC * 4 : 0;
+  static constexpr int kBytesSk = kScaledQK<QK> ? kBC * 4 : 0;
   // [K buf0][K buf1][V buf0][V buf1][sk buf0][sk buf1]
   static constexpr int kOffV = 2 * kBytesK;
   static constexpr int kOffSk = kOffV + 2 * kBytesV;
@@ -360,7 +363,7 @@ __device__ __forceinline__ void issue_k(char* smem, int w, int lane, int kb, int
     if (TL::kSegK % TL::kIssuers == 0 || w + i * TL::kIssuers < TL::kSegK)
       lds_load16<i * TL::kIssuers * 1024>(rsK, voffK[i], soff, base);
   });
-  if constexpr (QK == QK_I8) {
+  if constexpr (kScaledQK<QK>) {
     if (w == 0) {
       const i32x4 rsS = buffer_rsrc(sbase, (uint32_t)n * 4);
 #pragma unroll
@@ -454,10 +457,10 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
   // The first K tile streams in while this lane's Q row loads.
   if (group == 0)
     issue_k<D, QK, PV>(smem, wg, lane, 0, 0, head_ptr(p.k, bh, sizeof(QT)),
-                       QK == QK_I8 ? (const void*)(p.k_scale + (int64_t)bh * N) : nullptr, N, voff);
+                       kScaledQK<QK> ? (const void*)(p.k_scale + (int64_t)bh * N) : nullptr, N, voff);
 
   // ---- this lane's query row as the B operand of S^T = K Q^T (registers)
-  constexpr int QST = (QK == QK_BF16) ? D / 16 : (QK == QK_I8 ? D / 32 : D / 2);
+  constexpr int QST = (QK == QK_BF16) ? D / 16 : (kScaledQK<QK> ? D / 32 : D / 2);
   i32x4 qv[QK == QK_F32 ? 1 : QST];
   float qf[QK == QK_F32 ? QST : 1];
   float sq_log2 = 0.f;
@@ -475,7 +478,7 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
         const QT* src = Qg + (int64_t)row * D + 2 * EPC * t + EPC * g;
         qv[t] = ok ? *(const i32x4*)src : i32x4{0, 0, 0, 0};
       }
-      if constexpr (QK == QK_I8) sq_log2 = ok ? p.q_scale[(int64_t)b * N + row] * p.scale_log2 : 0.f;
+      if constexpr (kScaledQK<QK>) sq_log2 = ok ? p.q_scale[(int64_t)b * N + row] * p.scale_log2 : 0.f;
     }
   };
   load_q(bh, qrow);
@@ -724,6 +727,21 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
             for (int r = 0; r < 16; ++r)
               s[ks][r] = (float)acc[r] * (skt[32 * ks + key_of_reg(r, g)] * sq_log2);
           }
+        } else if constexpr (QK == QK_F8) {
+          // E4M3 codes in the int8 layout: two fp8 products per 32-byte
+          // chunk of the row, then the per-row scales as for int8
+          const float* skt = (const float*)(smem + TL::kOffSk + (jg & 1) * TL::kBytesSk);
+#pragma unroll
+          for (int ks = 0; ks < NKS; ++ks) {
+            const char* krow = kt + ks * 32 * TL::kStrK + k_lane + 16 * g;
+            f32x16 acc = {};
+#pragma unroll
+            for (int st = 0; st < QST; ++st)
+              acc = mfma_fp8x2(*(const i32x4*)(krow + 32 * st), qv[st], acc);
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              s[ks][r] = acc[r] * (skt[32 * ks + key_of_reg(r, g)] * sq_log2);
+          }
         } else {
 #pragma unroll
           for (int ks = 0; ks < NKS; ++ks) {
@@ -793,7 +811,7 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
     const float mraw_new = fmaxf(mraw_run, mx);
     // normaliser m of this block's probabilities P = exp2(s*c - m), in log2
     // units (int8: s is already scaled)
-    float m_use = (QK == QK_I8) ? mraw_new : mraw_new * p.scale_log2;
+    float m_use = kScaledQK<QK> ? mraw_new : mraw_new * p.scale_log2;
     if constexpr (STAB) {
       // Stabilised variant ("Why Low-Precision Transformer Training Fails",
       // Figure 7 and Algorithm 1): when the row maximum r_m occurs more than
@@ -824,7 +842,7 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
     for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        if constexpr (QK == QK_I8)
+        if constexpr (kScaledQK<QK>)
           s[ks][r] = exp2_approx(s[ks][r] - m_use);
         else
           s[ks][r] = exp2_approx(__builtin_fmaf(s[ks][r], p.scale_log2, -m_use));
@@ -927,7 +945,7 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
     const bool same = j + 1 < cur.nblk;
     const int b = same ? cur.bh : nxt.bh;
     return Prefetch{head_ptr(p.k, b, sizeof(QT)),
-                    QK == QK_I8 ? (const void*)(p.k_scale + (int64_t)b * N) : nullptr,
+                    kScaledQK<QK> ? (const void*)(p.k_scale + (int64_t)b * N) : nullptr,
                     same ? (j + 1) * BC : 0, (jg0 + j + 1) & 1, same || nxt.valid};
   };
   // the V block of local block j of the current tile
@@ -1042,6 +1060,9 @@ hipError_t launch_d(const AttnArgs& a, const FlashParams& fp, int64_t bh, int nt
                         : launch_c<D, QK_I8, PV_F32_VBF16, true>(fp, c, bh, nt, st);
       return a.p_bf16 ? launch_c<D, QK_I8, PV_BF16, false>(fp, c, bh, nt, st)
                       : launch_c<D, QK_I8, PV_F32_VBF16, false>(fp, c, bh, nt, st);
+    case kFP8:
+      return a.p_bf16 ? launch_c<D, QK_F8, PV_BF16, false>(fp, c, bh, nt, st)
+                      : launch_c<D, QK_F8, PV_F32_VBF16, false>(fp, c, bh, nt, st);
   }
   return hipErrorInvalidValue;
 }

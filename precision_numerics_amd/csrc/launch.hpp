@@ -7,7 +7,7 @@
 
 namespace pn {
 
-enum DType : int { kF32 = 0, kBF16 = 1, kINT8 = 2, kF64 = 3 };
+enum DType : int { kF32 = 0, kBF16 = 1, kINT8 = 2, kF64 = 3, kFP8 = 4 };
 
 struct AttnArgs {
   const void* q = nullptr;
@@ -63,5 +63,7 @@ hipError_t launch_delta(const void* o, const void* d_o, int out_dtype, int head_
 
 hipError_t launch_quantize(const float* x, int64_t rows, int64_t d,
                            int8_t* codes, float* scales, hipStream_t stream);
+hipError_t launch_quantize_fp8(const float* x, int64_t rows, int64_t d,
+                               uint8_t* codes, float* scales, hipStream_t stream);
 
 }  // namespace pn

@@ -184,3 +184,19 @@ def test_f64_is_not_an_attention_dtype(clib):
     out = B.AttnDeviation()
     assert clib.attn_deviation(FAKE, B.ATTN_F64, FAKE, 10, FAKE, 1 << 20, ctypes.byref(out),
                                None) == B.ATTN_ERR_INVALID_ARG
+
+
+def test_fp8_validation(clib):
+    p = _prob(dtype=B.ATTN_FP8)
+    assert clib.attn_fwd_flash(ctypes.byref(p), FAKE, FAKE, FAKE, None, None, FAKE, None,
+                               None) == B.ATTN_ERR_INVALID_ARG          # scales missing
+    assert "ATTN_FP8" in clib.attn_last_error().decode()
+    p = _prob(dtype=B.ATTN_FP8, stabilized=1, beta=2.0)
+    assert clib.attn_fwd_flash(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                               None) == B.ATTN_ERR_UNSUPPORTED
+    p = _prob(dtype=B.ATTN_FP8)
+    assert clib.attn_fwd_flash_debug_s(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                       None) == B.ATTN_ERR_UNSUPPORTED
+    assert clib.attn_quantize_fp8(FAKE, 4, 0, FAKE, FAKE, None) == 1
+    assert clib.attn_quantize_fp8(FAKE, 4, 2000, FAKE, FAKE, None) == 1
+    assert clib.attn_quantize_fp8(None, 0, 64, None, None, None) == 0
