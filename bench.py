@@ -33,7 +33,7 @@ if ROOT not in sys.path:
 import synth  # noqa: E402
 
 METRIC = "attn fwd TFLOP/s (bf16 causal, % MFMA peak) + max|err| vs FP64 oracle"
-PEAK = {"bf16": 2516.6, "int8": 5033.2, "f32": 157.3}     # dense MFMA, MI355X
+PEAK = {"bf16": 2516.6, "int8": 5033.2, "fp8": 5033.2, "f32": 157.3}  # dense MFMA, MI355X
 HBM_PEAK_GBS = 8000.0
 
 
@@ -414,6 +414,26 @@ def main():
                                  "hbm_frac": round(nb / (dms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
         except Exception as exc:                         # noqa: BLE001
             legs["bwd_delta"] = {"error": repr(exc)}
+        try:
+            log("bench: fp8 (E4M3) Q/K flash leg on the int8 workload's shape")
+            c5 = synth.CONFIGS["c5"]
+            in5 = synth.make_inputs(c5)
+            q8, qs8 = pna.attn_quantize_fp8(torch.from_numpy(in5.q).cuda())
+            k8, ks8 = pna.attn_quantize_fp8(torch.from_numpy(in5.k).cuda())
+            v8 = to_device(in5)[2]
+            o8 = torch.empty(q8.shape, dtype=torch.bfloat16, device="cuda")
+            fms = event_time_ms(lambda: pna.attn_fwd_flash(q8, k8, v8, causal=c5.causal,
+                                                           q_scale=qs8, k_scale=ks8, out=o8),
+                                20, 3)
+            f5 = c5.flops()
+            # QK^T at the fp8 peak, P*V at the bf16 peak
+            ideal = (f5 / 2 / (PEAK["fp8"] * 1e12) + f5 / 2 / (PEAK["bf16"] * 1e12)) * 1e3
+            legs["flash_fp8"] = {"workload": f"{c5.name} shape with E4M3 Q/K", "ms": round(fms, 4),
+                                 "tflops": round(f5 / (fms * 1e-3) / 1e12, 2),
+                                 "frac_of_fp8_bf16_peak": round(ideal / fms, 4)}
+            del q8, k8, v8, o8, in5
+        except Exception as exc:                         # noqa: BLE001
+            legs["flash_fp8"] = {"error": repr(exc)}
         try:
             log("bench: int8 quantiser leg")
             x = torch.randn(cfg.batch * cfg.heads * cfg.seq_len, cfg.head_dim, device="cuda")
