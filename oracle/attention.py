@@ -49,7 +49,7 @@ import numpy as np
 
 __all__ = [
     "default_scale", "attention", "attention_head", "int8_scores",
-    "attention_int8", "attention_int8_head", "quantize_int8", "deviation",
+    "attention_int8", "attention_int8_head", "quantize_int8", "quantize_int8_tiles", "deviation",
     "attention_probabilities", "attention_delta", "run_heads",
 ]
 
@@ -160,6 +160,34 @@ def quantize_int8(x) -> Tuple[np.ndarray, np.ndarray]:
     ratio = (x / scale[..., None]).astype(np.float32)
     codes = np.clip(np.rint(ratio), -127.0, 127.0).astype(np.int8)
     return codes, scale
+
+
+def quantize_int8_tiles(x, tile_rows: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Per-tile int8 quantisation of float32 x[..., n, d]: the rows of each
+    leading index are cut into tiles of ``tile_rows`` consecutive rows (the
+    last one ragged), and every tile shares one scale:
+      absmax_t = max over the tile's rows and columns of |x|
+      scale_t  = float32(absmax_t / 127), 1 if that is 0
+      code     = clamp(round_half_even(float32(x / scale_t)), -127, 127)
+    (the per-row rule of ``quantize_int8`` with a coarser scale granularity,
+    the per-block scales named among the pages' low-precision variants).
+    Returns (codes int8 [..., n, d], scales float32 [..., n]) with every row
+    carrying its tile's scale, so the int8 attention consumes them as is."""
+    x = np.asarray(x, dtype=np.float32)
+    assert tile_rows >= 1
+    n = x.shape[-2]
+    codes = np.empty(x.shape, dtype=np.int8)
+    scales = np.empty(x.shape[:-1], dtype=np.float32)
+    for r0 in range(0, n, tile_rows):
+        r1 = min(n, r0 + tile_rows)
+        tile = x[..., r0:r1, :]
+        absmax = np.max(np.abs(tile), axis=(-2, -1))
+        scale = (absmax / np.float32(127.0)).astype(np.float32)
+        scale = np.where(scale == np.float32(0.0), np.float32(1.0), scale).astype(np.float32)
+        ratio = (tile / scale[..., None, None]).astype(np.float32)
+        codes[..., r0:r1, :] = np.clip(np.rint(ratio), -127.0, 127.0).astype(np.int8)
+        scales[..., r0:r1] = scale[..., None]
+    return codes, scales
 
 
 def int8_scores(q_codes, k_codes) -> np.ndarray:

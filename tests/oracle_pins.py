@@ -559,3 +559,37 @@ def check_fp8_scores_and_attention(ora):
         o2, lse2 = ora.attention(qd, kd, v, causal=causal, scale=0.3)
         assert np.allclose(o, o2, rtol=1e-12, atol=1e-13)
         assert np.allclose(lse, lse2, rtol=1e-12, atol=1e-13)
+
+
+@pin
+def check_int8_tile_quantiser(ora):
+    """Per-tile int8 scales: one-row tiles reproduce the per-row quantiser,
+    whole-head tiles use the head's absmax, every tile's maximum maps to
+    +-127 with rows sharing its scale, tiles restart at every head, and a
+    hand-worked tile (scale 0.5: ties to even) gives its codes exactly."""
+    rng = _rng(73)
+    x = (rng.standard_normal((2, 3, 37, 20)) * np.exp(rng.standard_normal((2, 3, 37, 1)))
+         ).astype(np.float32)
+    c1, s1 = ora.quantize_int8_tiles(x, 1)
+    c0, s0 = ora.quantize_int8(x)
+    assert np.array_equal(c1, c0) and np.array_equal(s1, s0)
+    cn, sn = ora.quantize_int8_tiles(x, 10 ** 6)
+    head_max = np.abs(x).max(axis=(-2, -1))
+    assert np.array_equal(sn, np.repeat((head_max / np.float32(127))[..., None], 37, axis=-1))
+    for t in (4, 16):
+        ct, st = ora.quantize_int8_tiles(x, t)
+        for r0 in range(0, 37, t):
+            r1 = min(37, r0 + t)
+            tile_s = st[..., r0:r1]
+            assert np.all(tile_s == tile_s[..., :1])
+            amax = np.abs(ct[..., r0:r1, :].astype(np.int32)).max(axis=(-2, -1))
+            assert np.all(amax == 127)
+            assert np.array_equal(tile_s[..., 0],
+                                  (np.abs(x[..., r0:r1, :]).max(axis=(-2, -1)) / np.float32(127)))
+    y = np.zeros((1, 5, 2), dtype=np.float32)
+    y[0, :, 0] = [63.5, -0.25, 0.75, 1.25, 0.0]
+    y[0, :, 1] = [-63.5, 0.5, 20.0, -0.75, 0.0]
+    cy, sy = ora.quantize_int8_tiles(y, 2)   # tiles: rows 0-1, 2-3, 4
+    assert list(sy[0]) == [0.5, 0.5, np.float32(20.0) / np.float32(127), np.float32(20.0) / np.float32(127), 1.0]
+    assert list(cy[0, 0]) == [127, -127] and list(cy[0, 1]) == [0, 1]   # -0.5 -> 0, 1.0 -> 1
+    assert list(cy[0, 4]) == [0, 0]

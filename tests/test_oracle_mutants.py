@@ -50,11 +50,11 @@ MUTANTS = [
      "codes = np.clip(np.trunc(ratio), -127.0, 127.0)"),
     ("quantiser rounds half away", "codes = np.clip(np.rint(ratio), -127.0, 127.0)",
      "codes = np.clip(np.sign(ratio) * np.floor(np.abs(ratio) + 0.5), -127.0, 127.0)"),
-    ("quantiser divides by 128", "scale = (absmax / np.float32(127.0))",
-     "scale = (absmax / np.float32(128.0))"),
+    ("quantiser divides by 128", "\n    scale = (absmax / np.float32(127.0))",
+     "\n    scale = (absmax / np.float32(128.0))"),
     ("quantiser zero-row guard dropped",
-     "scale = np.where(scale == np.float32(0.0), np.float32(1.0), scale)",
-     "scale = np.where(scale == np.float32(0.0), np.float32(0.0), scale)"),
+     "\n    scale = np.where(scale == np.float32(0.0), np.float32(1.0), scale)",
+     "\n    scale = np.where(scale == np.float32(0.0), np.float32(0.0), scale)"),
     ("quantiser clamps at 128", "codes = np.clip(np.rint(ratio), -127.0, 127.0)",
      "codes = np.clip(np.rint(ratio * np.float32(128.0 / 127.0)), -128.0, 127.0)"),
     ("signed mean takes |e|", "mean_signed=float(ef.sum() / n_fin)",
@@ -70,6 +70,15 @@ MUTANTS = [
      "return prod[..., :-1].sum(axis=-1)"),
     ("delta adds instead of multiplying", "prod = g64 * o64", "prod = g64 + o64"),
     ("delta squares O", "prod = g64 * o64", "prod = o64 * o64"),
+    ("tile scale from the first row only", "absmax = np.max(np.abs(tile), axis=(-2, -1))",
+     "absmax = np.max(np.abs(tile[..., :1, :]), axis=(-2, -1))"),
+    ("ragged last tile dropped", "for r0 in range(0, n, tile_rows):",
+     "for r0 in range(0, max(n - tile_rows + 1, 1), tile_rows):"),
+    ("tile scale divides by 128",
+     "scale = (absmax / np.float32(127.0)).astype(np.float32)\n        scale = np.where",
+     "scale = (absmax / np.float32(128.0)).astype(np.float32)\n        scale = np.where"),
+    ("tile codes clamp at 128", "codes[..., r0:r1, :] = np.clip(np.rint(ratio), -127.0, 127.0)",
+     "codes[..., r0:r1, :] = np.clip(np.rint(ratio * np.float32(128 / 127)), -128.0, 127.0)"),
 ]
 
 
