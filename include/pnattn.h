@@ -229,6 +229,20 @@ attn_status_t attn_bwd_delta(const attn_problem_t* prob, const void* o,
 attn_status_t attn_quantize_int8(const float* x, int64_t rows, int64_t d,
                                  int8_t* codes, float* scales, void* stream);
 
+/* Per-tile int8 scales (the per-block scale granularity among the
+ * low-precision variants): x [groups][n][d] fp32, e.g. groups = batch*heads;
+ * the n rows of each group form tiles of tile_rows consecutive rows (the
+ * last one ragged, tiles never span two groups), and each tile shares
+ *   scale_t = fp32(absmax over the tile / 127)  (IEEE division), 1 if 0;
+ *   code    = clamp(round_half_even(fp32(x / scale_t)), -127, 127).
+ * codes: [groups][n][d] int8; scales: [groups][n] fp32, every row holding
+ * its tile's scale, so attn_fwd_flash/attn_fwd_baseline take them as the
+ * per-row scales of ATTN_INT8.  tile_rows = 1 is attn_quantize_int8.
+ * 1 <= d <= 1024, tile_rows >= 1; zero sizes validate and return ATTN_OK. */
+attn_status_t attn_quantize_int8_tiles(const float* x, int64_t groups, int64_t n,
+                                       int64_t d, int64_t tile_rows, int8_t* codes,
+                                       float* scales, void* stream);
+
 /* The same per-row scheme with E4M3 fp8 codes (ATTN_FP8; the per-row
  * absmax/448 scale is this library's reading, as for int8):
  *   scale_r = fp32(absmax_r / 448)  (IEEE division), 1 if that is 0;

@@ -83,6 +83,8 @@ _SIGNATURES = {
                        ctypes.POINTER(AttnDeviation), _P],
     "attn_quantize_int8": [_P, ctypes.c_int64, ctypes.c_int64, _P, _P, _P],
     "attn_quantize_fp8": [_P, ctypes.c_int64, ctypes.c_int64, _P, _P, _P],
+    "attn_quantize_int8_tiles": [_P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                 ctypes.c_int64, _P, _P, _P],
     "attn_bwd_delta": [ctypes.POINTER(AttnProblem), _P, _P, _P, _P],
     "attn_wasserstein_scratch_size": [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                       ctypes.POINTER(ctypes.c_size_t)],
@@ -261,6 +263,23 @@ def attn_quantize_int8(x, *, codes=None, scales=None, stream=None):
               if scales is None else scales)
     _check(load().attn_quantize_int8(_ptr(x), rows, d, _ptr(codes), _ptr(scales),
                                      _stream(stream)))
+    return codes, scales
+
+
+def attn_quantize_int8_tiles(x, tile_rows: int, *, codes=None, scales=None, stream=None):
+    """Per-tile int8 quantisation of fp32 x[..., n, d] (tiles of tile_rows
+    rows inside each leading index); returns (codes, per-row scales)."""
+    import torch
+    _contig(x, codes, scales)
+    if x.dtype != torch.float32 or x.dim() < 2:
+        raise TypeError("x must be float32 [..., n, d]")
+    n, d = x.shape[-2], x.shape[-1]
+    groups = x.numel() // (n * d) if n * d else 0
+    codes = torch.empty(x.shape, dtype=torch.int8, device=x.device) if codes is None else codes
+    scales = (torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
+              if scales is None else scales)
+    _check(load().attn_quantize_int8_tiles(_ptr(x), groups, n, d, int(tile_rows), _ptr(codes),
+                                           _ptr(scales), _stream(stream)))
     return codes, scales
 
 

@@ -315,6 +315,23 @@ attn_status_t attn_wasserstein(const void* a, int32_t a_dtype, const void* b, in
   return ok();
 }
 
+attn_status_t attn_quantize_int8_tiles(const float* x, int64_t groups, int64_t n, int64_t d,
+                                       int64_t tile_rows, int8_t* codes, float* scales,
+                                       void* stream) {
+  if (groups < 0 || n < 0) return fail(ATTN_ERR_INVALID_ARG, "groups and n must be >= 0");
+  if (d < 1 || d > 1024) return fail(ATTN_ERR_INVALID_ARG, "d must be in [1, 1024] (got %lld)", (long long)d);
+  if (tile_rows < 1) return fail(ATTN_ERR_INVALID_ARG, "tile_rows must be >= 1");
+  if (groups == 0 || n == 0) return ok();
+  if (x == nullptr || codes == nullptr || scales == nullptr)
+    return fail(ATTN_ERR_INVALID_ARG, "x, codes and scales must be non-NULL");
+  const int64_t tile = tile_rows < n ? tile_rows : n;
+  if (groups > INT32_MAX / ((n + tile - 1) / tile))
+    return fail(ATTN_ERR_UNSUPPORTED, "too many tiles");
+  return from_hip(pn::launch_quantize_tiles(x, groups, n, d, tile, codes, scales,
+                                            (hipStream_t)stream),
+                  "attn_quantize_int8_tiles launch");
+}
+
 attn_status_t attn_quantize_fp8(const float* x, int64_t rows, int64_t d, uint8_t* codes,
                                 float* scales, void* stream) {
   if (rows < 0) return fail(ATTN_ERR_INVALID_ARG, "rows must be >= 0");

@@ -63,6 +63,9 @@ hipError_t launch_delta(const void* o, const void* d_o, int out_dtype, int head_
 
 hipError_t launch_quantize(const float* x, int64_t rows, int64_t d,
                            int8_t* codes, float* scales, hipStream_t stream);
+hipError_t launch_quantize_tiles(const float* x, int64_t groups, int64_t n, int64_t d,
+                                 int64_t tile_rows, int8_t* codes, float* scales,
+                                 hipStream_t stream);
 hipError_t launch_quantize_fp8(const float* x, int64_t rows, int64_t d,
                                uint8_t* codes, float* scales, hipStream_t stream);
 

@@ -51,7 +51,46 @@ __global__ __launch_bounds__(256) void quantize_fp8_kernel(const float* x, int64
   if (lane == 0) scales[r] = sc;
 }
 
+// Per-tile int8 scales: the n rows of every group (a (batch, head)) are cut
+// into tiles of tile_rows rows, the last one ragged; one workgroup per tile
+// takes the tile's absmax (first pass), then writes the codes with the
+// shared scale and that scale for each of its rows (second pass).
+__global__ __launch_bounds__(256) void quantize_tiles_kernel(const float* x, int64_t n, int d,
+                                                            int64_t tile_rows, int64_t tiles_per,
+                                                            int8_t* codes, float* scales) {
+  __shared__ float red[4];
+  const int64_t t = blockIdx.x;
+  const int64_t grp = t / tiles_per;
+  const int64_t r0 = (t - grp * tiles_per) * tile_rows;
+  const int64_t r1 = r0 + tile_rows < n ? r0 + tile_rows : n;
+  const int64_t base = (grp * n + r0) * d;
+  const int64_t cnt = (r1 - r0) * d;
+  float am = 0.f;
+  for (int64_t i = threadIdx.x; i < cnt; i += 256) am = fmaxf(am, fabsf(x[base + i]));
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) am = fmaxf(am, __shfl_xor(am, off));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = am;
+  __syncthreads();
+  am = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  float sc = __fdiv_rn(am, 127.0f);
+  if (sc == 0.f) sc = 1.0f;
+  for (int64_t i = threadIdx.x; i < cnt; i += 256) {
+    const float q = fminf(fmaxf(rintf(__fdiv_rn(x[base + i], sc)), -127.f), 127.f);
+    codes[base + i] = (int8_t)(int)q;
+  }
+  for (int64_t r = r0 + threadIdx.x; r < r1; r += 256) scales[grp * n + r] = sc;
+}
+
 }  // namespace
+
+hipError_t launch_quantize_tiles(const float* x, int64_t groups, int64_t n, int64_t d,
+                                 int64_t tile_rows, int8_t* codes, float* scales,
+                                 hipStream_t st) {
+  const int64_t tiles_per = (n + tile_rows - 1) / tile_rows;
+  hipLaunchKernelGGL(quantize_tiles_kernel, dim3((unsigned)(groups * tiles_per)), dim3(256), 0,
+                     st, x, n, (int)d, tile_rows, tiles_per, codes, scales);
+  return hipGetLastError();
+}
 
 hipError_t launch_quantize_fp8(const float* x, int64_t rows, int64_t d, uint8_t* codes,
                                float* scales, hipStream_t st) {

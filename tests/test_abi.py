@@ -200,3 +200,13 @@ def test_fp8_validation(clib):
     assert clib.attn_quantize_fp8(FAKE, 4, 0, FAKE, FAKE, None) == 1
     assert clib.attn_quantize_fp8(FAKE, 4, 2000, FAKE, FAKE, None) == 1
     assert clib.attn_quantize_fp8(None, 0, 64, None, None, None) == 0
+
+
+def test_tile_quantiser_validation(clib):
+    Q = clib.attn_quantize_int8_tiles
+    assert Q(FAKE, 2, 16, 0, 4, FAKE, FAKE, None) == 1
+    assert Q(FAKE, 2, 16, 64, 0, FAKE, FAKE, None) == 1
+    assert Q(FAKE, -1, 16, 64, 4, FAKE, FAKE, None) == 1
+    assert Q(None, 2, 16, 64, 4, FAKE, FAKE, None) == 1
+    assert Q(None, 0, 16, 64, 4, None, None, None) == 0
+    assert Q(None, 2, 0, 64, 4, None, None, None) == 0

@@ -296,3 +296,31 @@ def test_full_workloads(lib, name, kernel, p_bf16, count):
             for u in units:
                 dots = oracle.int8_scores(oq.reshape(b * h, n, d)[u], okc.reshape(b * h, n, d)[u])
                 assert np.array_equal(s_all[u].cpu().numpy().astype(np.int64), dots)
+
+
+@pytest.mark.parametrize("tile_rows", [1, 7, 64, 256, 10 ** 6])
+def test_int8_tile_quantiser_and_attention(lib, tile_rows):
+    """Per-tile int8 scales: codes and per-row scales bit-exact with the
+    oracle's tile quantiser; flash and baseline on them match the oracle's
+    int8 attention (ragged n, both causal modes)."""
+    import precision_numerics_amd as pna
+    cfg = synth.small(synth.CONFIGS["c5"], batch=2, heads=3, seq_len=333, head_dim=64)
+    inp = synth.make_inputs(cfg, seed=88 + tile_rows % 97)
+    q32 = torch.from_numpy(inp.q).cuda()
+    k32 = torch.from_numpy(inp.k).cuda()
+    qc, qs = pna.attn_quantize_int8_tiles(q32, tile_rows)
+    kc, ks = pna.attn_quantize_int8_tiles(k32, tile_rows)
+    oqc, oqs = oracle.quantize_int8_tiles(inp.q, tile_rows)
+    okc, oks = oracle.quantize_int8_tiles(inp.k, tile_rows)
+    assert np.array_equal(qc.cpu().numpy(), oqc) and np.array_equal(qs.cpu().numpy(), oqs)
+    assert np.array_equal(kc.cpu().numpy(), okc) and np.array_equal(ks.cpu().numpy(), oks)
+    v = torch_bf16(inp.v)
+    vf = synth.bf16_bits_to_f32(inp.v).astype(np.float64)
+    for causal in (False, True):
+        ref, _ = oracle.attention_int8(oqc, oqs, okc, oks, vf, causal=causal)
+        o = pna.attn_fwd_flash(qc, kc, v, causal=causal, q_scale=qs, k_scale=ks)
+        ob, _ = pna.attn_fwd_baseline(qc, kc, v, causal=causal, q_scale=qs, k_scale=ks)
+        torch.cuda.synchronize()
+        _print(f"int8 tiles={tile_rows} causal={causal}")
+        assert_close(out_to_f64(o), ref, "bf16", f"flash tiles={tile_rows}")
+        assert_close(out_to_f64(ob), ref, "bf16", f"baseline tiles={tile_rows}")
