@@ -50,7 +50,7 @@ import numpy as np
 __all__ = [
     "default_scale", "attention", "attention_head", "int8_scores",
     "attention_int8", "attention_int8_head", "quantize_int8", "quantize_int8_tiles", "deviation",
-    "attention_probabilities", "attention_delta", "run_heads",
+    "attention_probabilities", "attention_delta", "attention_backward_head", "run_heads",
 ]
 
 
@@ -256,6 +256,35 @@ def attention_delta(o, d_o) -> np.ndarray:
     assert o64.shape == g64.shape
     prod = g64 * o64
     return prod.sum(axis=-1)
+
+
+def attention_backward_head(q, k, v, o, d_o, *, causal: bool, scale: float):
+    """Gradients (dQ, dK, dV) of one head's attention in float64, given the
+    stored forward output o and the upstream gradient d_o.
+
+    The chain rule through O = P V, P = row-softmax(S), S = scale Q K^T:
+        dV = P^T dO,  dP = dO V^T,
+        dS = P o (dP - delta 1^T),  delta = rowsum(dO o O)
+        dQ = scale dS K,  dK = scale dS^T Q
+    ("Why Low-Precision Transformer Training Fails": delta = rowsum(dO o O),
+    Figure 5 caption; the section isolating the error in O computes delta
+    from the stored low-precision O, so delta here is formed from the o
+    passed in; with the exact O this is the exact gradient, since
+    rowsum(dP o P) = rowsum(dO o O)).  P is recomputed exactly from q, k.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    o = np.asarray(o, dtype=np.float64)
+    g = np.asarray(d_o, dtype=np.float64)
+    p = attention_probabilities(q, k, causal=causal, scale=scale)
+    delta = (g * o).sum(axis=1)
+    dv = p.T @ g
+    dp = g @ v.T
+    ds = p * (dp - delta[:, None])
+    dq = scale * (ds @ k)
+    dk = scale * (ds.T @ q)
+    return dq, dk, dv
 
 
 # ---------------------------------------------------------------------------

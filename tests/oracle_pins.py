@@ -593,3 +593,72 @@ def check_int8_tile_quantiser(ora):
     assert list(sy[0]) == [0.5, 0.5, np.float32(20.0) / np.float32(127), np.float32(20.0) / np.float32(127), 1.0]
     assert list(cy[0, 0]) == [127, -127] and list(cy[0, 1]) == [0, 1]   # -0.5 -> 0, 1.0 -> 1
     assert list(cy[0, 4]) == [0, 0]
+
+
+# ---------------------------------------------------------------------------
+# attention backward (dQ, dK, dV)
+# ---------------------------------------------------------------------------
+
+def _torch_grads(q, k, v, g, causal, scale):
+    import torch
+    tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
+    s = scale * (tq @ tk.T)
+    if causal:
+        n = s.shape[0]
+        s = s.masked_fill(torch.triu(torch.ones(n, n, dtype=torch.bool), 1), float("-inf"))
+    out = torch.softmax(s, dim=1) @ tv
+    out.backward(torch.tensor(g, dtype=torch.float64))
+    return out.detach().numpy(), tq.grad.numpy(), tk.grad.numpy(), tv.grad.numpy()
+
+
+@pin
+def check_backward(ora):
+    """Gradients against torch float64 autograd of the plain attention (a
+    library routine), against central finite differences of
+    L = sum(dO o O), closed forms (each dS row sums to 0, so the dK rows sum
+    to 0; the dV rows sum to the dO rows; equal keys give dQ = 0), and the
+    stored-O reading: perturbing o by E shifts dQ and dK by exactly the
+    delta change rowsum(dO o E) and leaves dV alone."""
+    rng = _rng(83)
+    for causal in (False, True):
+        for n, d, dv_ in ((1, 3, 2), (5, 4, 3), (9, 6, 5)):
+            q = rng.standard_normal((n, d))
+            k = rng.standard_normal((n, d))
+            v = rng.standard_normal((n, dv_))
+            g = rng.standard_normal((n, dv_))
+            o, tq, tk, tv = _torch_grads(q, k, v, g, causal, 0.7)
+            dq, dk, dvv = ora.attention_backward_head(q, k, v, o, g, causal=causal, scale=0.7)
+            for a, b in ((dq, tq), (dk, tk), (dvv, tv)):
+                assert np.allclose(a, b, rtol=1e-10, atol=1e-12), np.abs(a - b).max()
+            assert np.allclose(dk.sum(axis=0), 0.0, atol=1e-12)
+            assert np.allclose(dvv.sum(axis=0), g.sum(axis=0), rtol=1e-12, atol=1e-12)
+            e = rng.standard_normal(o.shape) * 1e-3
+            dq2, dk2, dv2 = ora.attention_backward_head(q, k, v, o + e, g, causal=causal, scale=0.7)
+            p = ora.attention_probabilities(q, k, causal=causal, scale=0.7)
+            dd = (g * e).sum(axis=1)
+            assert np.allclose(dq2 - dq, -0.7 * (dd[:, None] * (p @ k)), rtol=1e-9, atol=1e-14)
+            assert np.allclose(dk2 - dk, -0.7 * ((p * dd[:, None]).T @ q), rtol=1e-9, atol=1e-14)
+            assert np.array_equal(dv2, dvv)
+    # central differences of L(q, k, v) = sum(g o O)
+    n, d = 6, 4
+    q, k, v, g = (rng.standard_normal((n, d)) for _ in range(4))
+    for causal in (False, True):
+        def loss(qq, kk, vv):
+            return float((g * ora.attention(qq, kk, vv, causal=causal, scale=0.9)[0]).sum())
+        o = ora.attention(q, k, v, causal=causal, scale=0.9)[0]
+        grads = ora.attention_backward_head(q, k, v, o, g, causal=causal, scale=0.9)
+        h = 1e-6
+        for which, grad in enumerate(grads):
+            for (i, j) in ((0, 0), (2, 3), (5, 1)):
+                args = [q.copy(), k.copy(), v.copy()]
+                args[which][i, j] += h
+                up = loss(*args)
+                args[which][i, j] -= 2 * h
+                dn = loss(*args)
+                fd = (up - dn) / (2 * h)
+                assert abs(fd - grad[i, j]) <= 1e-6 * max(1.0, abs(fd)), (which, i, j, fd, grad[i, j])
+    # equal keys: constant score rows, dQ = 0
+    kk = np.tile(rng.standard_normal((1, d)), (n, 1))
+    o = ora.attention(q, kk, v, causal=False, scale=0.9)[0]
+    dq, _, _ = ora.attention_backward_head(q, kk, v, o, g, causal=False, scale=0.9)
+    assert np.allclose(dq, 0.0, atol=1e-12)

@@ -70,6 +70,14 @@ MUTANTS = [
      "return prod[..., :-1].sum(axis=-1)"),
     ("delta adds instead of multiplying", "prod = g64 * o64", "prod = g64 + o64"),
     ("delta squares O", "prod = g64 * o64", "prod = o64 * o64"),
+    ("backward: dV without the transpose", "dv = p.T @ g", "dv = p @ g"),
+    ("backward: dS sign flipped", "ds = p * (dp - delta[:, None])", "ds = p * (delta[:, None] - dp)"),
+    ("backward: delta from O alone", "delta = (g * o).sum(axis=1)", "delta = (o * o).sum(axis=1)"),
+    ("backward: delta from dO alone", "delta = (g * o).sum(axis=1)", "delta = (g * g).sum(axis=1)"),
+    ("backward: dQ without the scale", "dq = scale * (ds @ k)", "dq = ds @ k"),
+    ("backward: dK from dS, not its transpose", "dk = scale * (ds.T @ q)",
+     "dk = scale * (ds @ q)"),
+    ("backward: dP without V transposed", "dp = g @ v.T", "dp = g @ v[::-1].T"),
     ("tile scale from the first row only", "absmax = np.max(np.abs(tile), axis=(-2, -1))",
      "absmax = np.max(np.abs(tile[..., :1, :]), axis=(-2, -1))"),
     ("ragged last tile dropped", "for r0 in range(0, n, tile_rows):",
