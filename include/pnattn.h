@@ -220,6 +220,32 @@ attn_status_t attn_wasserstein(const void* a, int32_t a_dtype, const void* b, in
 attn_status_t attn_bwd_delta(const attn_problem_t* prob, const void* o,
                              const void* d_o, float* delta, void* stream);
 
+/* Bytes of workspace attn_bwd_flash needs: delta, B*H*N fp32.           */
+attn_status_t attn_bwd_workspace_size(const attn_problem_t* prob, size_t* bytes);
+
+/* FlashAttention backward: the gradients of O = softmax_rows(S) V with
+ * S = scale Q K^T (causal mask as in the forward) for the upstream gradient
+ * dO, from the stored forward output O and its lse:
+ *   delta = rowsum(dO o O), dV = P^T dO, dP = dO V^T,
+ *   dS = P o (dP - delta), dQ = scale dS K, dK = scale dS^T Q
+ * ("Why Low-Precision Transformer Training Fails": delta = rowsum(dO o O),
+ * Figure 5 caption; delta is formed from the stored, low-precision O, as
+ * that page's analysis of the error in O has it).  P is recomputed from
+ * q, k and lse block by block (nothing N x N is stored).
+ *   prob   : as for the forward; ATTN_BF16 only (UNSUPPORTED otherwise),
+ *            standard variant (stabilized = 0); p_bf16 is not used (the
+ *            backward rounds P and dS to bf16 for its bf16 products)
+ *   q,k,v,o,d_o : [B,H,N,d] bf16 (o and lse from attn_fwd_flash)
+ *   lse    : [B,H,N] fp32, natural log, as attn_fwd_flash writes it
+ *   dq,dk,dv : [B,H,N,d] bf16 outputs (RNE of the fp32 accumulations)
+ *   workspace: attn_bwd_workspace_size bytes; holds delta afterwards.
+ * Deterministic: every output element is accumulated by one lane in a
+ * fixed order.                                                            */
+attn_status_t attn_bwd_flash(const attn_problem_t* prob, const void* q, const void* k,
+                             const void* v, const void* o, const void* d_o, const float* lse,
+                             void* dq, void* dk, void* dv, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
 /* Symmetric per-row int8 quantisation of fp32 rows x [rows][d] (the int8
  * Q/K input of "INT-FlashAttention", abstract; the per-row absmax/127
  * granularity is this library's reading):

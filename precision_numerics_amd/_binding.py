@@ -86,6 +86,9 @@ _SIGNATURES = {
     "attn_quantize_int8_tiles": [_P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                  ctypes.c_int64, _P, _P, _P],
     "attn_bwd_delta": [ctypes.POINTER(AttnProblem), _P, _P, _P, _P],
+    "attn_bwd_workspace_size": [ctypes.POINTER(AttnProblem), ctypes.POINTER(ctypes.c_size_t)],
+    "attn_bwd_flash": [ctypes.POINTER(AttnProblem), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                       ctypes.c_size_t, _P],
     "attn_wasserstein_scratch_size": [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                       ctypes.POINTER(ctypes.c_size_t)],
     "attn_wasserstein": [_P, ctypes.c_int32, _P, ctypes.c_int32, ctypes.c_int64, _P,
@@ -340,6 +343,31 @@ def attn_wasserstein(a, b, *, scratch=None, stream=None) -> dict:
                                    scratch.numel() * scratch.element_size(), ctypes.byref(res),
                                    _stream(stream)))
     return res.as_dict()
+
+
+def attn_bwd_workspace_size(prob: AttnProblem) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load().attn_bwd_workspace_size(ctypes.byref(prob), ctypes.byref(n)))
+    return n.value
+
+
+def attn_bwd_flash(q, k, v, o, d_o, lse, *, causal: bool, softmax_scale: float = 0.0,
+                   dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """FlashAttention backward (bf16); returns (dq, dk, dv)."""
+    import torch
+    _contig(q, k, v, o, d_o, lse, dq, dk, dv, workspace)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    prob = make_problem(q, causal=causal, softmax_scale=softmax_scale)
+    need = attn_bwd_workspace_size(prob)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(load().attn_bwd_flash(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                                 _ptr(d_o), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+                                 _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                 _stream(stream)))
+    return dq, dk, dv
 
 
 def attn_version() -> str:

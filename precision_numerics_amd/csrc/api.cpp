@@ -158,6 +158,56 @@ attn_status_t attn_bwd_delta(const attn_problem_t* prob, const void* o, const vo
                   "attn_bwd_delta launch");
 }
 
+attn_status_t attn_bwd_workspace_size(const attn_problem_t* prob, size_t* bytes) {
+  if (bytes == nullptr) return fail(ATTN_ERR_INVALID_ARG, "bytes is NULL");
+  pn::AttnArgs a;
+  bool empty = false;
+  const void* fake = (const void*)prob;  // sizes only: pointers are not checked here
+  attn_status_t st = check_problem(prob, fake, fake, fake, nullptr, nullptr, fake, &a, &empty);
+  if (st != ATTN_OK) return st;
+  *bytes = empty ? 0 : (size_t)(prob->batch * prob->heads * prob->seq_len) * sizeof(float);
+  return ok();
+}
+
+attn_status_t attn_bwd_flash(const attn_problem_t* prob, const void* q, const void* k,
+                             const void* v, const void* o, const void* d_o, const float* lse,
+                             void* dq, void* dk, void* dv, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  pn::AttnArgs a;
+  bool empty = false;
+  attn_status_t st = check_problem(prob, q, k, v, nullptr, nullptr, o, &a, &empty);
+  if (st != ATTN_OK) return st;
+  if (prob->dtype != ATTN_BF16)
+    return fail(ATTN_ERR_UNSUPPORTED, "attn_bwd_flash is built for ATTN_BF16 only");
+  if (prob->stabilized != 0)
+    return fail(ATTN_ERR_UNSUPPORTED, "attn_bwd_flash is the standard variant's backward");
+  if (empty) return ok();
+  if (d_o == nullptr || lse == nullptr || dq == nullptr || dk == nullptr || dv == nullptr ||
+      workspace == nullptr)
+    return fail(ATTN_ERR_INVALID_ARG, "d_o, lse, dq, dk, dv and workspace must be non-NULL");
+  const size_t need = (size_t)(prob->batch * prob->heads * prob->seq_len) * sizeof(float);
+  if (workspace_bytes < need)
+    return fail(ATTN_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+  pn::AttnBwdArgs b;
+  b.q = q;
+  b.k = k;
+  b.v = v;
+  b.o = o;
+  b.d_o = d_o;
+  b.lse = lse;
+  b.delta = (float*)workspace;
+  b.dq = dq;
+  b.dk = dk;
+  b.dv = dv;
+  b.batch = prob->batch;
+  b.heads = prob->heads;
+  b.seq_len = prob->seq_len;
+  b.head_dim = (int)prob->head_dim;
+  b.causal = prob->causal;
+  b.scale = a.scale;
+  return from_hip(pn::launch_flash_bwd(b, (hipStream_t)stream), "attn_bwd_flash launch");
+}
+
 attn_status_t attn_fwd_flash(const attn_problem_t* prob, const void* q, const void* k,
                              const void* v, const float* q_scale, const float* k_scale,
                              void* o, float* lse, void* stream) {

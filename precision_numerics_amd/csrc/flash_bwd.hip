@@ -1,0 +1,309 @@
+// FlashAttention backward for bf16 on gfx950: dQ, dK, dV from Q, K, V, the
+// stored output O, its upstream gradient dO and the forward's log-sum-exp.
+//
+// Chain rule through O = P V, P = row-softmax(S), S = scale Q K^T:
+//   dV = P^T dO,  dP = dO V^T,  dS = P o (dP - delta),  delta = rowsum(dO o O)
+//   dQ = scale dS K,  dK = scale dS^T Q
+// ("Why Low-Precision Transformer Training Fails": delta = rowsum(dO o O) in
+// the Figure 5 caption; the section isolating the error in O forms delta
+// from the stored low-precision O, as here).  P is recomputed block by
+// block as exp2(scale log2(e) q.k - lse log2(e)) from the forward's lse, so
+// no N x N matrix is stored.
+//
+// Precision (the usual bf16 FlashAttention backward): the products run on
+// bf16 MFMA with fp32 accumulation; P is rounded to bf16 for dV and dS for
+// dQ and dK; P, dP, dS themselves are fp32; dQ, dK, dV leave as bf16 (RNE).
+//
+// Two deterministic kernels (no atomics: every output element is summed by
+// one lane in a fixed order):
+//   dq kernel : a workgroup owns 128 query rows (32 per wave, a lane per
+//               query) and walks the key blocks: S^T = K Q^T and
+//               dP^T = V dO^T (K and V rows fed in a permuted order so that
+//               accumulator register r of lane group g holds key
+//               16(r/8) + 8g + r%8, the order the dS^T operand of the next
+//               product needs), then dQ^T += K^T dS^T with K^T read
+//               through the transposing LDS read.
+//   dkv kernel: a workgroup owns 128 key rows (a lane per key) and walks the
+//               query blocks: S = Q K^T and dP = dO V^T with permuted query
+//               rows, then dV^T += dO^T P and dK^T += Q^T dS.
+// Tiles of 64 rows are staged in LDS with plain 16-byte loads (zeros past
+// N); the per-row lse and delta of a query block sit in LDS beside them.
+#include "device.hpp"
+#include "launch.hpp"
+
+namespace pn {
+namespace {
+
+constexpr int kThreads = 256;   // four waves
+constexpr int kTile = 128;      // rows a workgroup owns (32 per wave)
+constexpr int kStep = 64;       // rows of the other operand per step
+
+struct BwdParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* d_o;
+  const float* lse;
+  const float* delta;
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  int n;
+  int tiles;          // 128-row tiles per head
+  float scale;
+  float scale_log2;   // scale * log2(e)
+};
+
+// Row m of a 32-row A operand carries element perm_row(m) of its subtile;
+// then accumulator register r of lane group g holds element elem_of_reg(r, g).
+__device__ __forceinline__ int perm_row(int m) {
+  return 16 * (m >> 4) + 8 * ((m >> 2) & 1) + 4 * ((m >> 3) & 1) + (m & 3);
+}
+__device__ __forceinline__ int elem_of_reg(int r, int g) { return 16 * (r >> 3) + 8 * g + (r & 7); }
+
+template <int D> struct Geo {
+  static constexpr int kRow = D * 2;         // bf16 row bytes
+  static constexpr int kStr = kRow + 64;     // padded LDS row stride
+  static constexpr int kBytes = kStep * kStr;
+  static constexpr int QST = D / 16;         // 16-element chunks of a row
+  static constexpr int DT = D / 32;          // 32-row subtiles of a transposed output
+};
+
+// rows r0.. r0+63 of a [N][D] bf16 matrix into an LDS tile (zeros past N)
+template <int D>
+__device__ __forceinline__ void stage(char* lds, const uint16_t* src, int r0, int N) {
+  constexpr int kPerRow = D * 2 / 16;
+  for (int c = threadIdx.x; c < kStep * kPerRow; c += kThreads) {
+    const int row = c / kPerRow, col = c - row * kPerRow;
+    i32x4 x = {0, 0, 0, 0};
+    if (r0 + row < N) x = *(const i32x4*)(src + (int64_t)(r0 + row) * D + col * 8);
+    *(i32x4*)(lds + row * Geo<D>::kStr + col * 16) = x;
+  }
+}
+
+// a row of the B operand (16 bytes per 16-element chunk, lane group g holds
+// elements 8g..8g+7 of each chunk)
+template <int D>
+__device__ __forceinline__ void load_row(i32x4 (&dst)[Geo<D>::QST], const uint16_t* row, bool ok,
+                                         int g) {
+#pragma unroll
+  for (int t = 0; t < Geo<D>::QST; ++t)
+    dst[t] = ok ? *(const i32x4*)(row + 16 * t + 8 * g) : i32x4{0, 0, 0, 0};
+}
+
+// store 32 lanes' transposed accumulators (register r of tile dt: element
+// 32 dt + 8(r/4) + 4g + r%4 of this lane's row), times `mul`, as bf16
+template <int D>
+__device__ __forceinline__ void store_row(uint16_t* dst, const f32x16 (&acc)[Geo<D>::DT],
+                                          float mul, int g) {
+#pragma unroll
+  for (int dt = 0; dt < Geo<D>::DT; ++dt)
+#pragma unroll
+    for (int b4 = 0; b4 < 4; ++b4) {
+      const int d0 = 32 * dt + 8 * b4 + 4 * g;
+      uint2 w;
+      w.x = (uint32_t)f32_to_bf16(acc[dt][4 * b4 + 0] * mul) |
+            ((uint32_t)f32_to_bf16(acc[dt][4 * b4 + 1] * mul) << 16);
+      w.y = (uint32_t)f32_to_bf16(acc[dt][4 * b4 + 2] * mul) |
+            ((uint32_t)f32_to_bf16(acc[dt][4 * b4 + 3] * mul) << 16);
+      *(uint2*)(dst + d0) = w;
+    }
+}
+
+// lanes' LDS byte offsets: permuted A-operand rows, and the transposing read
+template <int D>
+__device__ __forceinline__ int row_lane(int n) { return perm_row(n) * Geo<D>::kStr; }
+template <int D>
+__device__ __forceinline__ int tr_lane(int lane) {
+  const int g = lane >> 5;
+  return (8 * g + ((lane & 15) >> 2)) * Geo<D>::kStr + (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdParams p) {
+  using G = Geo<D>;
+  __shared__ __attribute__((aligned(16))) char smem[2 * G::kBytes];  // K block, V block
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 5, n = lane & 31;
+  const int N = p.n;
+  const int64_t bh = blockIdx.x / p.tiles;
+  const int q0 = (int)(blockIdx.x - bh * p.tiles) * kTile;
+  const int qrow = q0 + wave * 32 + n;
+  const bool qok = qrow < N;
+  const int64_t hoff = bh * (int64_t)N * D;
+  i32x4 qv[G::QST], gv[G::QST];
+  load_row<D>(qv, p.q + hoff + (int64_t)qrow * D, qok, g);
+  load_row<D>(gv, p.d_o + hoff + (int64_t)qrow * D, qok, g);
+  const float lse2 = qok ? p.lse[bh * N + qrow] * kLog2e : 0.f;
+  const float dlt = qok ? p.delta[bh * N + qrow] : 0.f;
+  f32x16 dq[G::DT];
+#pragma unroll
+  for (int dt = 0; dt < G::DT; ++dt) dq[dt] = f32x16{};
+  const int kend = CAUSAL ? min(N, q0 + kTile) : N;
+  const int a_off = row_lane<D>(n) + 16 * g;
+  const int t_off = tr_lane<D>(lane);
+  for (int kb = 0; kb < kend; kb += kStep) {
+    __syncthreads();
+    stage<D>(smem, p.k + hoff, kb, N);
+    stage<D>(smem + G::kBytes, p.v + hoff, kb, N);
+    __syncthreads();
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      s[ks] = f32x16{};
+      dp[ks] = f32x16{};
+      const char* kr = smem + ks * 32 * G::kStr + a_off;
+      const char* vr = smem + G::kBytes + ks * 32 * G::kStr + a_off;
+#pragma unroll
+      for (int t = 0; t < G::QST; ++t) {
+        s[ks] = mfma_bf16(__builtin_bit_cast(bf16x8, *(const i32x4*)(kr + 32 * t)),
+                          __builtin_bit_cast(bf16x8, qv[t]), s[ks]);
+        dp[ks] = mfma_bf16(__builtin_bit_cast(bf16x8, *(const i32x4*)(vr + 32 * t)),
+                           __builtin_bit_cast(bf16x8, gv[t]), dp[ks]);
+      }
+    }
+    // dS^T as the B operand of the next product: keys 16u + 8g + e
+    bf16x8 dsb[kStep / 16];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = kb + 32 * ks + elem_of_reg(r, g);
+        const bool vis = key < N && (!CAUSAL || key <= qrow);
+        const float pv = vis ? exp2_approx(s[ks][r] * p.scale_log2 - lse2) : 0.f;
+        dsb[2 * ks + (r >> 3)][r & 7] = (__bf16)(pv * (dp[ks][r] - dlt));
+      }
+#pragma unroll
+    for (int u = 0; u < kStep / 16; ++u)
+#pragma unroll
+      for (int dt = 0; dt < G::DT; ++dt) {
+        const char* src = smem + t_off + 16 * u * G::kStr + 64 * dt;
+        const i16x4 lo = lds_read_tr16(src);
+        const i16x4 hi = lds_read_tr16(src + 4 * G::kStr);
+        dq[dt] = mfma_bf16(join_bf16x8(lo, hi), dsb[u], dq[dt]);
+      }
+  }
+  if (qok) store_row<D>(p.dq + hoff + (int64_t)qrow * D, dq, p.scale, g);
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads) void bwd_dkv_kernel(BwdParams p) {
+  using G = Geo<D>;
+  // Q block, dO block, then the block's lse * log2(e) and delta
+  __shared__ __attribute__((aligned(16))) char smem[2 * G::kBytes + 2 * kStep * 4];
+  float* lse_t = (float*)(smem + 2 * G::kBytes);
+  float* dlt_t = lse_t + kStep;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 5, n = lane & 31;
+  const int N = p.n;
+  const int64_t bh = blockIdx.x / p.tiles;
+  const int k0 = (int)(blockIdx.x - bh * p.tiles) * kTile;
+  const int krow = k0 + wave * 32 + n;
+  const bool kok = krow < N;
+  const int64_t hoff = bh * (int64_t)N * D;
+  i32x4 kv[G::QST], vv[G::QST];
+  load_row<D>(kv, p.k + hoff + (int64_t)krow * D, kok, g);
+  load_row<D>(vv, p.v + hoff + (int64_t)krow * D, kok, g);
+  f32x16 dk[G::DT], dv[G::DT];
+#pragma unroll
+  for (int dt = 0; dt < G::DT; ++dt) {
+    dk[dt] = f32x16{};
+    dv[dt] = f32x16{};
+  }
+  const int a_off = row_lane<D>(n) + 16 * g;
+  const int t_off = tr_lane<D>(lane);
+  // causal: queries below this tile's first key see none of its keys
+  for (int qb = CAUSAL ? k0 : 0; qb < N; qb += kStep) {
+    __syncthreads();
+    stage<D>(smem, p.q + hoff, qb, N);
+    stage<D>(smem + G::kBytes, p.d_o + hoff, qb, N);
+    if (threadIdx.x < kStep) {
+      const int qi = qb + (int)threadIdx.x;
+      lse_t[threadIdx.x] = qi < N ? p.lse[bh * N + qi] * kLog2e : 0.f;
+      dlt_t[threadIdx.x] = qi < N ? p.delta[bh * N + qi] : 0.f;
+    }
+    __syncthreads();
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs) {
+      s[qs] = f32x16{};
+      dp[qs] = f32x16{};
+      const char* qr = smem + qs * 32 * G::kStr + a_off;
+      const char* gr = smem + G::kBytes + qs * 32 * G::kStr + a_off;
+#pragma unroll
+      for (int t = 0; t < G::QST; ++t) {
+        s[qs] = mfma_bf16(__builtin_bit_cast(bf16x8, *(const i32x4*)(qr + 32 * t)),
+                          __builtin_bit_cast(bf16x8, kv[t]), s[qs]);
+        dp[qs] = mfma_bf16(__builtin_bit_cast(bf16x8, *(const i32x4*)(gr + 32 * t)),
+                           __builtin_bit_cast(bf16x8, vv[t]), dp[qs]);
+      }
+    }
+    // P and dS as B operands: queries 16u + 8g + e of the block
+    bf16x8 pb[kStep / 16], dsb[kStep / 16];
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int qi = 32 * qs + elem_of_reg(r, g);
+        const bool vis = qb + qi < N && (!CAUSAL || krow <= qb + qi);
+        const float pv = vis ? exp2_approx(s[qs][r] * p.scale_log2 - lse_t[qi]) : 0.f;
+        pb[2 * qs + (r >> 3)][r & 7] = (__bf16)pv;
+        dsb[2 * qs + (r >> 3)][r & 7] = (__bf16)(pv * (dp[qs][r] - dlt_t[qi]));
+      }
+#pragma unroll
+    for (int u = 0; u < kStep / 16; ++u)
+#pragma unroll
+      for (int dt = 0; dt < G::DT; ++dt) {
+        const char* qsrc = smem + t_off + 16 * u * G::kStr + 64 * dt;
+        const char* gsrc = smem + G::kBytes + t_off + 16 * u * G::kStr + 64 * dt;
+        dv[dt] = mfma_bf16(join_bf16x8(lds_read_tr16(gsrc), lds_read_tr16(gsrc + 4 * G::kStr)),
+                           pb[u], dv[dt]);
+        dk[dt] = mfma_bf16(join_bf16x8(lds_read_tr16(qsrc), lds_read_tr16(qsrc + 4 * G::kStr)),
+                           dsb[u], dk[dt]);
+      }
+  }
+  if (kok) {
+    store_row<D>(p.dk + hoff + (int64_t)krow * D, dk, p.scale, g);
+    store_row<D>(p.dv + hoff + (int64_t)krow * D, dv, 1.0f, g);
+  }
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_bwd_dc(const BwdParams& bp, int64_t bh, hipStream_t st) {
+  const dim3 grid((unsigned)(bh * bp.tiles));
+  hipLaunchKernelGGL((bwd_dkv_kernel<D, CAUSAL>), grid, dim3(kThreads), 0, st, bp);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), grid, dim3(kThreads), 0, st, bp);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_flash_bwd(const AttnBwdArgs& a, hipStream_t st) {
+  const int64_t bh = a.batch * a.heads;
+  const int64_t rows = bh * a.seq_len;
+  hipError_t e = launch_delta(a.o, a.d_o, kBF16, a.head_dim, rows, a.delta, st);
+  if (e != hipSuccess) return e;
+  BwdParams bp;
+  bp.q = (const uint16_t*)a.q;
+  bp.k = (const uint16_t*)a.k;
+  bp.v = (const uint16_t*)a.v;
+  bp.d_o = (const uint16_t*)a.d_o;
+  bp.lse = a.lse;
+  bp.delta = a.delta;
+  bp.dq = (uint16_t*)a.dq;
+  bp.dk = (uint16_t*)a.dk;
+  bp.dv = (uint16_t*)a.dv;
+  bp.n = (int)a.seq_len;
+  bp.tiles = (int)((a.seq_len + kTile - 1) / kTile);
+  bp.scale = a.scale;
+  bp.scale_log2 = (float)((double)a.scale * 1.4426950408889634);
+  if (a.head_dim == 64)
+    return a.causal ? launch_bwd_dc<64, true>(bp, bh, st) : launch_bwd_dc<64, false>(bp, bh, st);
+  if (a.head_dim == 128)
+    return a.causal ? launch_bwd_dc<128, true>(bp, bh, st) : launch_bwd_dc<128, false>(bp, bh, st);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pn

@@ -46,6 +46,26 @@ hipError_t launch_deviation(const void* o_test, int o_dtype,
                             const double* o_ref, int64_t n, void* scratch,
                             DeviationRecord* out_host, hipStream_t stream);
 
+// FlashAttention backward (bf16): delta = rowsum(dO o O) into `delta`
+// (B*H*N fp32, caller's workspace), then dK/dV and dQ.
+struct AttnBwdArgs {
+  const void* q = nullptr;
+  const void* k = nullptr;
+  const void* v = nullptr;
+  const void* o = nullptr;
+  const void* d_o = nullptr;
+  const float* lse = nullptr;
+  float* delta = nullptr;
+  void* dq = nullptr;
+  void* dk = nullptr;
+  void* dv = nullptr;
+  int64_t batch = 0, heads = 0, seq_len = 0;
+  int head_dim = 0;
+  int causal = 0;
+  float scale = 0.f;
+};
+hipError_t launch_flash_bwd(const AttnBwdArgs& a, hipStream_t stream);
+
 // Wasserstein distances of two n-element tensors (kF32, kBF16 or kF64):
 // sorted keys and partials live in scratch; the record holds the sums.
 struct WassersteinRecord {

@@ -210,3 +210,23 @@ def test_tile_quantiser_validation(clib):
     assert Q(None, 2, 16, 64, 4, FAKE, FAKE, None) == 1
     assert Q(None, 0, 16, 64, 4, None, None, None) == 0
     assert Q(None, 2, 0, 64, 4, None, None, None) == 0
+
+
+def test_backward_validation(clib):
+    p = _prob()
+    n = ctypes.c_size_t(0)
+    assert clib.attn_bwd_workspace_size(ctypes.byref(p), ctypes.byref(n)) == 0
+    assert n.value == 1 * 2 * 16 * 4
+    BW = clib.attn_bwd_flash
+    args = [FAKE] * 10       # q, k, v, o, d_o, lse, dq, dk, dv, workspace
+    assert BW(ctypes.byref(p), *args[:5], None, *args[6:], 1 << 20, None) == 1       # lse NULL
+    assert BW(ctypes.byref(p), *args[:9], None, 1 << 20, None) == 1                   # workspace NULL
+    assert BW(ctypes.byref(p), *args, 8, None) == 3                                   # too small
+    p8 = _prob(dtype=B.ATTN_INT8)
+    assert BW(ctypes.byref(p8), *args, 1 << 20, None) == 1                            # scales
+    pf = _prob(dtype=B.ATTN_F32)
+    assert BW(ctypes.byref(pf), *args, 1 << 20, None) == 2
+    ps = _prob(stabilized=1, beta=2.0)
+    assert BW(ctypes.byref(ps), *args, 1 << 20, None) == 2
+    empty = _prob(seq_len=0)
+    assert BW(ctypes.byref(empty), *([None] * 10), 0, None) == 0
