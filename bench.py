@@ -414,6 +414,29 @@ def main():
                                  "hbm_frac": round(nb / (dms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
         except Exception as exc:                         # noqa: BLE001
             legs["bwd_delta"] = {"error": repr(exc)}
+        if cfg.dtype == "bf16":
+            try:
+                log("bench: flash backward leg")
+                lse_b = torch.empty(q.shape[:-1], dtype=torch.float32, device="cuda")
+                pna.attn_fwd_flash(q, k, v, causal=cfg.causal, out=out, lse=lse_b)
+                g_b = torch.randn(out.shape, device="cuda").to(out.dtype)
+                dq_b, dk_b, dv_b = (torch.empty_like(x) for x in (q, k, v))
+                wsb = torch.empty(pna.attn_bwd_workspace_size(pna.make_problem(q, causal=cfg.causal)),
+                                  dtype=torch.uint8, device="cuda")
+                bwd_ms = event_time_ms(lambda: pna.attn_bwd_flash(
+                    q, k, v, out, g_b, lse_b, causal=cfg.causal, dq=dq_b, dk=dk_b, dv=dv_b,
+                    workspace=wsb), 5, 1)
+                # the usual accounting: five matrix products against the forward's two
+                bflops = 2.5 * flops
+                legs["flash_backward"] = {"ms": round(bwd_ms, 3),
+                                          "tflops": round(bflops / (bwd_ms * 1e-3) / 1e12, 2),
+                                          "frac_of_bf16_peak": round(
+                                              bflops / (bwd_ms * 1e-3) / 1e12 / PEAK["bf16"], 4),
+                                          "note": "2.5x the forward's flops; includes the delta "
+                                                  "kernel"}
+                del dq_b, dk_b, dv_b, wsb, g_b
+            except Exception as exc:                     # noqa: BLE001
+                legs["flash_backward"] = {"error": repr(exc)}
         try:
             log("bench: fp8 (E4M3) Q/K flash leg on the int8 workload's shape")
             c5 = synth.CONFIGS["c5"]
