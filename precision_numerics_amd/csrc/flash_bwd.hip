@@ -26,8 +26,9 @@
 //   dkv kernel: a workgroup owns 128 key rows (a lane per key) and walks the
 //               query blocks: S = Q K^T and dP = dO V^T with permuted query
 //               rows, then dV^T += dO^T P and dK^T += Q^T dS.
-// Tiles of 64 rows are staged in LDS with plain 16-byte loads (zeros past
-// N); the per-row lse and delta of a query block sit in LDS beside them.
+// Tiles of 64 rows are staged in LDS through registers, the next block's
+// global loads overlapping the current block's products (zeros past N);
+// the per-row lse and delta of a query block sit in LDS beside them.
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -69,17 +70,33 @@ template <int D> struct Geo {
   static constexpr int DT = D / 32;          // 32-row subtiles of a transposed output
 };
 
-// rows r0.. r0+63 of a [N][D] bf16 matrix into an LDS tile (zeros past N)
-template <int D>
-__device__ __forceinline__ void stage(char* lds, const uint16_t* src, int r0, int N) {
-  constexpr int kPerRow = D * 2 / 16;
-  for (int c = threadIdx.x; c < kStep * kPerRow; c += kThreads) {
-    const int row = c / kPerRow, col = c - row * kPerRow;
-    i32x4 x = {0, 0, 0, 0};
-    if (r0 + row < N) x = *(const i32x4*)(src + (int64_t)(r0 + row) * D + col * 8);
-    *(i32x4*)(lds + row * Geo<D>::kStr + col * 16) = x;
+// A 64-row block of a [N][D] bf16 matrix moves to LDS in two parts: fetch
+// (16-byte global loads into this thread's registers, zeros past N), issued
+// before the products of the current block so that the loads overlap them,
+// and commit (the registers into the padded LDS tile) after the next
+// barrier.
+template <int D> struct Staged {
+  static constexpr int kPerRow = D * 2 / 16;
+  static constexpr int kPer = kStep * kPerRow / kThreads;  // chunks per thread
+  i32x4 x[kPer];
+  __device__ __forceinline__ void fetch(const uint16_t* src, int r0, int N) {
+#pragma unroll
+    for (int c = 0; c < kPer; ++c) {
+      const int idx = (int)threadIdx.x + c * kThreads;
+      const int row = idx / kPerRow, col = idx - row * kPerRow;
+      x[c] = r0 + row < N ? *(const i32x4*)(src + (int64_t)(r0 + row) * D + col * 8)
+                          : i32x4{0, 0, 0, 0};
+    }
   }
-}
+  __device__ __forceinline__ void commit(char* lds) const {
+#pragma unroll
+    for (int c = 0; c < kPer; ++c) {
+      const int idx = (int)threadIdx.x + c * kThreads;
+      const int row = idx / kPerRow, col = idx - row * kPerRow;
+      *(i32x4*)(lds + row * Geo<D>::kStr + col * 16) = x[c];
+    }
+  }
+};
 
 // a row of the B operand (16 bytes per 16-element chunk, lane group g holds
 // elements 8g..8g+7 of each chunk)
@@ -142,11 +159,18 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdParams p) {
   const int kend = CAUSAL ? min(N, q0 + kTile) : N;
   const int a_off = row_lane<D>(n) + 16 * g;
   const int t_off = tr_lane<D>(lane);
+  Staged<D> sk, sv;
+  sk.fetch(p.k + hoff, 0, N);
+  sv.fetch(p.v + hoff, 0, N);
   for (int kb = 0; kb < kend; kb += kStep) {
     __syncthreads();
-    stage<D>(smem, p.k + hoff, kb, N);
-    stage<D>(smem + G::kBytes, p.v + hoff, kb, N);
+    sk.commit(smem);
+    sv.commit(smem + G::kBytes);
     __syncthreads();
+    if (kb + kStep < kend) {
+      sk.fetch(p.k + hoff, kb + kStep, N);
+      sv.fetch(p.v + hoff, kb + kStep, N);
+    }
     f32x16 s[2], dp[2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
@@ -213,16 +237,27 @@ __global__ __launch_bounds__(kThreads) void bwd_dkv_kernel(BwdParams p) {
   const int a_off = row_lane<D>(n) + 16 * g;
   const int t_off = tr_lane<D>(lane);
   // causal: queries below this tile's first key see none of its keys
-  for (int qb = CAUSAL ? k0 : 0; qb < N; qb += kStep) {
+  const int qstart = CAUSAL ? k0 : 0;
+  Staged<D> sq, sg;
+  float pl = 0.f, pd = 0.f;  // the block's lse * log2(e) and delta (threads < 64)
+  auto fetch = [&](int qb) __attribute__((always_inline)) {
+    sq.fetch(p.q + hoff, qb, N);
+    sg.fetch(p.d_o + hoff, qb, N);
+    const int qi = qb + (int)threadIdx.x;
+    pl = threadIdx.x < kStep && qi < N ? p.lse[bh * N + qi] * kLog2e : 0.f;
+    pd = threadIdx.x < kStep && qi < N ? p.delta[bh * N + qi] : 0.f;
+  };
+  fetch(qstart);
+  for (int qb = qstart; qb < N; qb += kStep) {
     __syncthreads();
-    stage<D>(smem, p.q + hoff, qb, N);
-    stage<D>(smem + G::kBytes, p.d_o + hoff, qb, N);
+    sq.commit(smem);
+    sg.commit(smem + G::kBytes);
     if (threadIdx.x < kStep) {
-      const int qi = qb + (int)threadIdx.x;
-      lse_t[threadIdx.x] = qi < N ? p.lse[bh * N + qi] * kLog2e : 0.f;
-      dlt_t[threadIdx.x] = qi < N ? p.delta[bh * N + qi] : 0.f;
+      lse_t[threadIdx.x] = pl;
+      dlt_t[threadIdx.x] = pd;
     }
     __syncthreads();
+    if (qb + kStep < N) fetch(qb + kStep);
     f32x16 s[2], dp[2];
 #pragma unroll
     for (int qs = 0; qs < 2; ++qs) {
