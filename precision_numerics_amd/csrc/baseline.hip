@@ -127,7 +127,11 @@ __device__ __forceinline__ float block_reduce(float x, bool is_max, float* red) 
 
 // SMODE: 0 scores already scaled (fp32), 1 int32 products of int8 codes,
 // 2 fp32 products of E4M3 codes; 1 and 2 apply scale * sq_i * sk_j here.
-template <int SMODE, bool PBF16>
+// CACHE > 0 (rows of at most CACHE * kThreads entries): each thread keeps
+// its scores in registers, so the row is read from HBM once instead of
+// three times; the order of every operation is the same either way, so
+// both forms give the same bits.
+template <int SMODE, bool PBF16, int CACHE>
 __global__ __launch_bounds__(kThreads) void softmax_kernel(const void* sp, void* pp,
                                                           const float* q_scale,
                                                           const float* k_scale, int N,
@@ -146,20 +150,45 @@ __global__ __launch_bounds__(kThreads) void softmax_kernel(const void* sp, void*
     else
       return ((const float*)sp)[row + j];
   };
-  float m = -INFINITY;
-  for (int j = threadIdx.x; j < jend; j += kThreads) m = fmaxf(m, score(j));
-  m = block_reduce(m, true, red);
-  float sum = 0.f;
-  for (int j = threadIdx.x; j < jend; j += kThreads)
-    sum += exp2_approx((score(j) - m) * kLog2e);
-  sum = block_reduce(sum, false, red);
-  const float inv = 1.f / sum;
-  for (int j = threadIdx.x; j < N; j += kThreads) {
-    const float pv = j < jend ? exp2_approx((score(j) - m) * kLog2e) * inv : 0.f;
+  auto store = [&](int j, float pv) {
     if constexpr (PBF16)
       ((uint16_t*)pp)[row + j] = f32_to_bf16(pv);
     else
       ((float*)pp)[row + j] = pv;
+  };
+  float m = -INFINITY;
+  if constexpr (CACHE > 0) {
+    float x[CACHE];
+#pragma unroll
+    for (int c = 0; c < CACHE; ++c) {
+      const int j = (int)threadIdx.x + c * kThreads;
+      x[c] = j < jend ? score(j) : -INFINITY;
+      m = fmaxf(m, x[c]);
+    }
+    m = block_reduce(m, true, red);
+    float sum = 0.f;
+#pragma unroll
+    for (int c = 0; c < CACHE; ++c) {
+      x[c] = exp2_approx((x[c] - m) * kLog2e);  // 0 past jend
+      if ((int)threadIdx.x + c * kThreads < jend) sum += x[c];
+    }
+    sum = block_reduce(sum, false, red);
+    const float inv = 1.f / sum;
+#pragma unroll
+    for (int c = 0; c < CACHE; ++c) {
+      const int j = (int)threadIdx.x + c * kThreads;
+      if (j < N) store(j, j < jend ? x[c] * inv : 0.f);
+    }
+  } else {
+    for (int j = threadIdx.x; j < jend; j += kThreads) m = fmaxf(m, score(j));
+    m = block_reduce(m, true, red);
+    float sum = 0.f;
+    for (int j = threadIdx.x; j < jend; j += kThreads)
+      sum += exp2_approx((score(j) - m) * kLog2e);
+    sum = block_reduce(sum, false, red);
+    const float inv = 1.f / sum;
+    for (int j = threadIdx.x; j < N; j += kThreads)
+      store(j, j < jend ? exp2_approx((score(j) - m) * kLog2e) * inv : 0.f);
   }
 }
 
@@ -303,6 +332,25 @@ hipError_t launch_pv(const AttnArgs& a, const void* p, hipStream_t st) {
   return hipGetLastError();
 }
 
+template <int CACHE>
+hipError_t launch_softmax(int mode, const AttnArgs& a, const void* s, void* p, dim3 grid,
+                          hipStream_t st) {
+  const int N = (int)a.seq_len;
+  if (mode == 1 && a.p_bf16)
+    hipLaunchKernelGGL((softmax_kernel<1, true, CACHE>), grid, dim3(kThreads), 0, st, s, p, a.q_scale, a.k_scale, N, a.causal, a.scale);
+  else if (mode == 1)
+    hipLaunchKernelGGL((softmax_kernel<1, false, CACHE>), grid, dim3(kThreads), 0, st, s, p, a.q_scale, a.k_scale, N, a.causal, a.scale);
+  else if (mode == 2 && a.p_bf16)
+    hipLaunchKernelGGL((softmax_kernel<2, true, CACHE>), grid, dim3(kThreads), 0, st, s, p, a.q_scale, a.k_scale, N, a.causal, a.scale);
+  else if (mode == 2)
+    hipLaunchKernelGGL((softmax_kernel<2, false, CACHE>), grid, dim3(kThreads), 0, st, s, p, a.q_scale, a.k_scale, N, a.causal, a.scale);
+  else if (a.p_bf16)
+    hipLaunchKernelGGL((softmax_kernel<0, true, CACHE>), grid, dim3(kThreads), 0, st, s, p, a.q_scale, a.k_scale, N, a.causal, a.scale);
+  else
+    hipLaunchKernelGGL((softmax_kernel<0, false, CACHE>), grid, dim3(kThreads), 0, st, s, p, a.q_scale, a.k_scale, N, a.causal, a.scale);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 size_t baseline_workspace_bytes(int64_t bh, int64_t n, int p_bf16) {
@@ -319,18 +367,13 @@ hipError_t launch_baseline(const AttnArgs& a, void* workspace, hipStream_t st) {
   if (e != hipSuccess) return e;
   dim3 grid2((unsigned)N, (unsigned)bh);
   const int mode = a.dtype == kINT8 ? 1 : (a.dtype == kFP8 ? 2 : 0);
-  if (mode == 1 && a.p_bf16)
-    hipLaunchKernelGGL((softmax_kernel<1, true>), grid2, dim3(kThreads), 0, st, s, p, a.q_scale, a.k_scale, N, a.causal, a.scale);
-  else if (mode == 1)
-    hipLaunchKernelGGL((softmax_kernel<1, false>), grid2, dim3(kThreads), 0, st, s, p, a.q_scale, a.k_scale, N, a.causal, a.scale);
-  else if (mode == 2 && a.p_bf16)
-    hipLaunchKernelGGL((softmax_kernel<2, true>), grid2, dim3(kThreads), 0, st, s, p, a.q_scale, a.k_scale, N, a.causal, a.scale);
-  else if (mode == 2)
-    hipLaunchKernelGGL((softmax_kernel<2, false>), grid2, dim3(kThreads), 0, st, s, p, a.q_scale, a.k_scale, N, a.causal, a.scale);
-  else if (a.p_bf16)
-    hipLaunchKernelGGL((softmax_kernel<0, true>), grid2, dim3(kThreads), 0, st, s, p, a.q_scale, a.k_scale, N, a.causal, a.scale);
+  if (N <= 8 * kThreads)
+    e = launch_softmax<8>(mode, a, s, p, grid2, st);
+  else if (N <= 32 * kThreads)
+    e = launch_softmax<32>(mode, a, s, p, grid2, st);
   else
-    hipLaunchKernelGGL((softmax_kernel<0, false>), grid2, dim3(kThreads), 0, st, s, p, a.q_scale, a.k_scale, N, a.causal, a.scale);
+    e = launch_softmax<0>(mode, a, s, p, grid2, st);
+  if (e != hipSuccess) return e;
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   return a.head_dim == 64 ? launch_pv<64>(a, p, st) : launch_pv<128>(a, p, st);

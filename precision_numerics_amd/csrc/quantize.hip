@@ -81,6 +81,60 @@ __global__ __launch_bounds__(256) void quantize_tiles_kernel(const float* x, int
   for (int64_t r = r0 + threadIdx.x; r < r1; r += 256) scales[grp * n + r] = sc;
 }
 
+// The per-row int8 and E4M3 quantisers for rows of d = 4 * LPR elements:
+// LPR lanes per row, one 16-byte load and one 4-byte store per lane, so a
+// wave covers 64 / LPR rows.  Same arithmetic per element as the kernels
+// above (bit-identical codes and scales).
+template <int LPR, bool FP8>
+__global__ __launch_bounds__(256) void quantize_vec_kernel(const float* x, int64_t rows,
+                                                          void* codes, float* scales) {
+  constexpr int d = 4 * LPR;
+  const int lane = threadIdx.x & 63;
+  const int64_t r = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * (64 / LPR) + lane / LPR;
+  const int sub = lane % LPR;
+  const bool ok = r < rows;
+  float4 v = ok ? *(const float4*)(x + r * d + 4 * sub) : make_float4(0.f, 0.f, 0.f, 0.f);
+  float am = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+#pragma unroll
+  for (int off = LPR / 2; off >= 1; off >>= 1) am = fmaxf(am, __shfl_xor(am, off));
+  float sc = __fdiv_rn(am, FP8 ? 448.0f : 127.0f);
+  if (sc == 0.f) sc = 1.0f;
+  if (!ok) return;
+  uint32_t packed;
+  if constexpr (FP8) {
+    packed = (uint32_t)f32_to_e4m3(__fdiv_rn(v.x, sc)) |
+             ((uint32_t)f32_to_e4m3(__fdiv_rn(v.y, sc)) << 8) |
+             ((uint32_t)f32_to_e4m3(__fdiv_rn(v.z, sc)) << 16) |
+             ((uint32_t)f32_to_e4m3(__fdiv_rn(v.w, sc)) << 24);
+  } else {
+    auto q = [&](float t) {
+      return (uint32_t)(uint8_t)(int8_t)(int)fminf(fmaxf(rintf(__fdiv_rn(t, sc)), -127.f), 127.f);
+    };
+    packed = q(v.x) | (q(v.y) << 8) | (q(v.z) << 16) | (q(v.w) << 24);
+  }
+  ((uint32_t*)codes)[(r * d) / 4 + sub] = packed;
+  if (sub == 0) scales[r] = sc;
+}
+
+template <bool FP8>
+bool launch_vec(const float* x, int64_t rows, int64_t d, void* codes, float* scales,
+                hipStream_t st) {
+  // 16-byte loads and 4-byte stores need aligned rows
+  if ((uintptr_t)x % 16 != 0 || (uintptr_t)codes % 4 != 0) return false;
+  if (d != 64 && d != 128 && d != 256) return false;
+  const int64_t per_block = 4 * (64 / (d / 4));
+  const dim3 grid((unsigned)((rows + per_block - 1) / per_block));
+  if (d == 64)
+    hipLaunchKernelGGL((quantize_vec_kernel<16, FP8>), grid, dim3(256), 0, st, x, rows, codes, scales);
+  else if (d == 128)
+    hipLaunchKernelGGL((quantize_vec_kernel<32, FP8>), grid, dim3(256), 0, st, x, rows, codes, scales);
+  else if (d == 256)
+    hipLaunchKernelGGL((quantize_vec_kernel<64, FP8>), grid, dim3(256), 0, st, x, rows, codes, scales);
+  else
+    return false;
+  return true;
+}
+
 }  // namespace
 
 hipError_t launch_quantize_tiles(const float* x, int64_t groups, int64_t n, int64_t d,
@@ -94,6 +148,7 @@ hipError_t launch_quantize_tiles(const float* x, int64_t groups, int64_t n, int6
 
 hipError_t launch_quantize_fp8(const float* x, int64_t rows, int64_t d, uint8_t* codes,
                                float* scales, hipStream_t st) {
+  if (launch_vec<true>(x, rows, d, codes, scales, st)) return hipGetLastError();
   const int64_t blocks = (rows + 3) / 4;
   hipLaunchKernelGGL(quantize_fp8_kernel, dim3((unsigned)blocks), dim3(256), 0, st, x, rows,
                      (int)d, codes, scales);
@@ -102,6 +157,7 @@ hipError_t launch_quantize_fp8(const float* x, int64_t rows, int64_t d, uint8_t*
 
 hipError_t launch_quantize(const float* x, int64_t rows, int64_t d, int8_t* codes,
                            float* scales, hipStream_t st) {
+  if (launch_vec<false>(x, rows, d, codes, scales, st)) return hipGetLastError();
   const int64_t blocks = (rows + 3) / 4;
   hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)blocks), dim3(256), 0, st, x, rows, (int)d,
                      codes, scales);
