@@ -541,6 +541,23 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
           lds_address(smem) + rq.buf * TL::kBytesK + wg * 1024);
   };
 
+  // The fp8 engine runs out of registers when the source offsets of this
+  // wave's segments stay live through the loop: the compiler then spills
+  // them, and each reload's wait also waits for the loads already in flight.
+  // There they are recomputed at the point of use (the opaque lane keeps the
+  // computation from being hoisted back out); the other engines keep them,
+  // since the recomputation costs vector instructions in the matrix
+  // half-step.
+  constexpr bool kFreshVoff = QK == QK_F8;
+  auto fresh_voff = [&](uint32_t (&dst)[TL::kSegPerWave]) __attribute__((always_inline)) {
+    int l = lane;
+    asm volatile("" : "+v"(l));
+#pragma unroll
+    for (int i = 0; i < TL::kSegPerWave; ++i)
+      dst[i] = group == 0 ? seg_src_offset(wg + i * TL::kIssuers, l, TL::kRowK, TL::kStrK)
+                          : seg_src_offset(wg + i * TL::kIssuers, l, TL::kRowV, TL::kStrV);
+  };
+
   auto m_body = [&](const int jl, const int jg, auto do_pv_c, auto do_s_c, auto issue_c,
                     const Prefetch& rq) __attribute__((always_inline)) {
     constexpr bool DO_PV = decltype(do_pv_c)::value;
@@ -550,7 +567,13 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
     constexpr int ISSUE = decltype(issue_c)::value;
     constexpr int NSEG = TL::kSegKPerWave;
     if constexpr (ISSUE == 2) {
-      if (rq.on) issue_v<D, QK, PV>(smem, wg, rq.kb, rq.buf, rq.base, N, voff);
+      if constexpr (!kFreshVoff) {
+        if (rq.on) issue_v<D, QK, PV>(smem, wg, rq.kb, rq.buf, rq.base, N, voff);
+      } else {
+        uint32_t vo[TL::kSegPerWave];
+        fresh_voff(vo);
+        if (rq.on) issue_v<D, QK, PV>(smem, wg, rq.kb, rq.buf, rq.base, N, vo);
+      }
     }
     if constexpr (PV == PV_BF16 && QK == QK_BF16) {
       // The whole half-step in program order, fenced so that the scheduler
@@ -631,7 +654,13 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
         }
     } else {
       if constexpr (ISSUE == 1) {
-        if (rq.on) issue_k<D, QK, PV>(smem, wg, lane, rq.kb, rq.buf, rq.base, rq.sbase, N, voff);
+        if constexpr (!kFreshVoff) {
+          if (rq.on) issue_k<D, QK, PV>(smem, wg, lane, rq.kb, rq.buf, rq.base, rq.sbase, N, voff);
+        } else {
+          uint32_t vo[TL::kSegPerWave];
+          fresh_voff(vo);
+          if (rq.on) issue_k<D, QK, PV>(smem, wg, lane, rq.kb, rq.buf, rq.base, rq.sbase, N, vo);
+        }
       }
       if constexpr (DO_PV) {
         const char* vt = (const char*)smem + TL::kOffV + ((jg - 1) & 1) * TL::kBytesV;
