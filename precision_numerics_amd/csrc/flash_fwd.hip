@@ -502,7 +502,7 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
   f32x16 oacc[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x16{};
-  float s[NKS][16];                                          // S_j, then P_j (fp32)
+  f32x16 s[NKS];                                             // S_j, then P_j (fp32)
   bf16x8 pb[PV == PV_BF16 ? BC / 16 : 1];                    // P_j as the bf16 operand
   float pf[PV == PV_BF16 ? 1 : NKS][PV == PV_BF16 ? 1 : 16];  // P_j for the fp32 engines
 #pragma unroll
@@ -593,9 +593,12 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
       const char* k0 = (const char*)smem + (jg & 1) * TL::kBytesK + k_lane + 16 * g;
       i16x4 vlo[NPV > 0 ? NPV : 1], vhi[NPV > 0 ? NPV : 1];
       i32x4 kf[NSM > 0 ? NSM : 1];
-      f32x16 acc[NKS];
+      // the S products accumulate straight into the score registers X
+      // reads (a separate accumulator made the compiler copy all of them)
+      if constexpr (DO_S) {
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) acc[ks] = f32x16{};
+        for (int ks = 0; ks < NKS; ++ks) s[ks] = f32x16{};
+      }
       auto load = [&](const int i) __attribute__((always_inline)) {
         if (i < NPV) {
           const char* src = vl + 16 * (i / DT) * TL::kStrV + 64 * (i % DT);
@@ -611,8 +614,8 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
           oacc[i % DT] = mfma_bf16(join_bf16x8(vlo[i], vhi[i]), pb[i / DT], oacc[i % DT]);
         } else {
           const int t = i - NPV;
-          acc[t / QST] = mfma_bf16(__builtin_bit_cast(bf16x8, kf[t]),
-                                   __builtin_bit_cast(bf16x8, qv[t % QST]), acc[t / QST]);
+          s[t / QST] = mfma_bf16(__builtin_bit_cast(bf16x8, kf[t]),
+                                 __builtin_bit_cast(bf16x8, qv[t % QST]), s[t / QST]);
         }
       };
       // The wave sharing this SIMD runs its softmax meanwhile; a dense VALU
@@ -637,7 +640,7 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
       __builtin_amdgcn_s_setprio(0);
       if constexpr (DO_S) {
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) pin(acc[ks]);
+        for (int ks = 0; ks < NKS; ++ks) pin(s[ks]);  // raw q.k; scaled inside exp2
       }
       if constexpr (DO_PV) {
 #pragma unroll
@@ -645,13 +648,10 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
       }
 #pragma unroll
       for (int u = 0; u < BC / 16; ++u) forget(pb[u]);
+      if constexpr (!DO_S) {
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          if constexpr (DO_S) s[ks][r] = acc[ks][r];  // raw q.k; scaled inside exp2
-          else forget(s[ks][r]);
-        }
+        for (int ks = 0; ks < NKS; ++ks) forget(s[ks]);
+      }
     } else {
       if constexpr (ISSUE == 1) {
         if constexpr (!kFreshVoff) {
@@ -706,9 +706,7 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
       }
       if constexpr (!DO_S) {
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) forget(s[ks][r]);
+        for (int ks = 0; ks < NKS; ++ks) forget(s[ks]);
       }
       if constexpr (DO_S) {
         const char* kt = (const char*)smem + (jg & 1) * TL::kBytesK;
