@@ -236,7 +236,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+        print(f"bench.py: the benchmark runs on one GPU only (asked for --gpus {args.gpus}); "
               "the kernels shard by (batch, head) with no exchange, so N GPUs would each run "
               "this one-GPU workload on their share", file=sys.stderr)
         sys.exit(2)
