@@ -1010,7 +1010,15 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
       half_x(0);
       __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
       block_barrier();
-      for (int j = 1; j < cur.nblk; ++j) {
+      // Causal tiles: when the last key block lies wholly above group 0's
+      // rows (the tile's first half), every score of it is masked for this
+      // group, so P = 0 adds nothing to O and m, l stay as they are.  Group 0
+      // then skips that block's S products, its softmax and its P.V
+      // products, passing the same barriers (and still issuing the next
+      // tile's loads).  Its waves' SIMD partners run those slots alone.
+      const int nb = cur.nblk;
+      const bool skip_last = CAUSAL && nb >= 2 && (nb - 1) * BC > cur.q0 + kBR / 2 - 1;
+      for (int j = 1; j < nb - (skip_last ? 1 : 0); ++j) {
         m_body(j, jg0 + j, kYes, kYes, kIssueK, next_k(j));
         block_barrier();
         x_prologue(j);
@@ -1018,7 +1026,15 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         block_barrier();
       }
-      m_body(cur.nblk, jg0 + cur.nblk, kYes, kNo, kIssueNone, kNone);
+      if (skip_last) {
+        m_body(nb - 1, jg0 + nb - 1, kYes, kNo, kIssueK, next_k(nb - 1));
+        block_barrier();
+        x_prologue(nb - 1);
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        block_barrier();
+      } else {
+        m_body(nb, jg0 + nb, kYes, kNo, kIssueNone, kNone);
+      }
       block_barrier();
       const bool more = nxt.valid;
       advance();
