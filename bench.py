@@ -47,9 +47,9 @@ TRAFFIC_SOURCES = ("precision_numerics_amd/csrc/flash_fwd.hip",
                    "precision_numerics_amd/csrc/launch.hpp")
 TRAFFIC = {
     "workload": "c3",
-    "sources_sha256": "ac649a5af85f77a007153c8a7dbb2613f2d2673694ddbd456018fb0b252e7296",
-    "fetch_kib": 293265.2, "fetch_scale": 2.0,
-    "write_kib": 135936.8, "write_scale": 1.0,
+    "sources_sha256": "d42dec3adb2b344c4fb1bf8cb4c0d6da7c66e8a7616ca6b33bbd03923777d89c",
+    "fetch_kib": 299897.0, "fetch_scale": 2.0,
+    "write_kib": 138760.4, "write_scale": 1.0,
 }
 
 
