@@ -489,11 +489,12 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
   // every iteration, which would also drain the K/V prefetch.
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
-  // Every wave runs all nblk blocks of its workgroup.  Near the causal
-  // diagonal a block can lie entirely above a wave's rows: its scores are all
-  // masked, so m and l are unchanged (exp(m - m') = 1) and P = 0 adds
-  // nothing to O.  Running it keeps the loop free of per-wave conditions,
-  // whose merging paths would keep dead score registers alive.
+  // Near the causal diagonal a block can lie entirely above a wave's rows:
+  // its scores are all masked, so m and l are unchanged (exp(m - m') = 1)
+  // and P = 0 adds nothing to O.  Inside the main loop every wave still runs
+  // such blocks, which keeps the loop free of per-wave conditions whose
+  // merging paths would keep dead score registers alive; only the last
+  // block of a tile is skipped, group-wide, after the loop (see the slots).
 
   float m_run = -INFINITY;     // normaliser of the accumulated block sums, log2 units
   float mraw_run = -INFINITY;  // running max of the unscaled scores

@@ -12,7 +12,8 @@
 // fp64: 8): negative values have all bits inverted, non-negative ones the
 // sign bit set, so unsigned key order is numeric order.  Every pass is
 //   histogram: workgroup g counts the digits of its contiguous chunk
-//   scan:      one workgroup turns the digit-major counts into offsets
+//   offsets:   per digit, the keys of smaller digits plus a scan of that
+//              digit's per-chunk counts
 //   scatter:   workgroup g walks its chunk in 256-element tiles; an element's
 //              rank among equal digits of its wave comes from eight ballots,
 //              the waves' counts are prefix-summed per digit in LDS, and the
@@ -94,30 +95,35 @@ __global__ __launch_bounds__(kThreads) void digit_histogram(const K* keys, int64
   counts[(int64_t)threadIdx.x * gridDim.x + blockIdx.x] = h[threadIdx.x];
 }
 
-// exclusive prefix sum of m = 256 * G counts (one workgroup of 1024 threads)
+// offsets[d * G + g] = number of keys with a smaller digit, plus those with
+// digit d in chunks before g: workgroup d sums the counts of all smaller
+// digits and scans its own G <= 1024 counts (one per thread).  Integer sums:
+// exact in any order.
 constexpr int kScanThreads = 1024;
-__global__ __launch_bounds__(kScanThreads) void exclusive_scan(const uint32_t* counts, int m,
-                                                               uint32_t* offsets) {
+__global__ __launch_bounds__(kScanThreads) void digit_offsets(const uint32_t* counts, int G,
+                                                              uint32_t* offsets) {
   __shared__ uint32_t part[kScanThreads];
-  const int per = (m + kScanThreads - 1) / kScanThreads;
-  const int lo = threadIdx.x * per;
-  const int hi = lo + per < m ? lo + per : m;
-  uint32_t s = 0;
-  for (int i = lo; i < hi; ++i) s += counts[i];
-  part[threadIdx.x] = s;
+  __shared__ uint32_t red[kScanThreads / 64];
+  const int d = blockIdx.x, t = threadIdx.x;
+  uint32_t below = 0;
+  for (int i = t; i < d * G; i += kScanThreads) below += counts[i];
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) below += __shfl_xor(below, off);
+  if ((t & 63) == 0) red[t >> 6] = below;
+  const uint32_t c = t < G ? counts[d * G + t] : 0u;
+  part[t] = c;
   __syncthreads();
-  // Hillis-Steele inclusive scan of the per-thread sums
+  uint32_t base = 0;
+#pragma unroll
+  for (int w = 0; w < kScanThreads / 64; ++w) base += red[w];
+  // Hillis-Steele inclusive scan of this digit's counts
   for (int off = 1; off < kScanThreads; off <<= 1) {
-    const uint32_t v = threadIdx.x >= (unsigned)off ? part[threadIdx.x - off] : 0u;
+    const uint32_t v = t >= off ? part[t - off] : 0u;
     __syncthreads();
-    part[threadIdx.x] += v;
+    part[t] += v;
     __syncthreads();
   }
-  uint32_t run = threadIdx.x == 0 ? 0u : part[threadIdx.x - 1];
-  for (int i = lo; i < hi; ++i) {
-    offsets[i] = run;
-    run += counts[i];
-  }
+  if (t < G) offsets[d * G + t] = base + part[t] - c;
 }
 
 // stable scatter of chunk g by the digit at `shift`
@@ -282,8 +288,7 @@ hipError_t sort_keys(const void* x, int64_t n, char* scratch, size_t off0, size_
   for (int shift = 0; shift < (int)(8 * sizeof(K)); shift += 8) {
     hipLaunchKernelGGL((digit_histogram<K>), dim3(G), dim3(kThreads), 0, st, buf[cur], n, chunk,
                        shift, counts);
-    hipLaunchKernelGGL(exclusive_scan, dim3(1), dim3(kScanThreads), 0, st, counts, 256 * G,
-                       offsets);
+    hipLaunchKernelGGL(digit_offsets, dim3(256), dim3(kScanThreads), 0, st, counts, G, offsets);
     hipLaunchKernelGGL((digit_scatter<K>), dim3(G), dim3(kThreads), 0, st, buf[cur], n, chunk,
                        shift, offsets, buf[cur ^ 1]);
     e = hipGetLastError();
