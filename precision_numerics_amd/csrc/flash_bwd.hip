@@ -37,7 +37,12 @@ namespace {
 
 constexpr int kThreads = 256;   // four waves
 constexpr int kTile = 128;      // rows a workgroup owns (32 per wave)
-constexpr int kStep = 64;       // rows of the other operand per step
+// Rows of the other operand per step: 32 for the dq kernel, whose registers
+// then fit two workgroups per compute unit (two waves per SIMD, one
+// covering the other's latencies), 64 for the dkv kernel, whose two output
+// accumulators keep it at one wave per SIMD anyway.
+constexpr int kStepDq = 32;
+constexpr int kStepDkv = 64;
 
 struct BwdParams {
   const uint16_t* q;
@@ -62,10 +67,10 @@ __device__ __forceinline__ int perm_row(int m) {
 }
 __device__ __forceinline__ int elem_of_reg(int r, int g) { return 16 * (r >> 3) + 8 * g + (r & 7); }
 
-template <int D> struct Geo {
+template <int D, int STEP> struct Geo {
   static constexpr int kRow = D * 2;         // bf16 row bytes
   static constexpr int kStr = kRow + 64;     // padded LDS row stride
-  static constexpr int kBytes = kStep * kStr;
+  static constexpr int kBytes = STEP * kStr;
   static constexpr int QST = D / 16;         // 16-element chunks of a row
   static constexpr int DT = D / 32;          // 32-row subtiles of a transposed output
 };
@@ -75,9 +80,9 @@ template <int D> struct Geo {
 // before the products of the current block so that the loads overlap them,
 // and commit (the registers into the padded LDS tile) after the next
 // barrier.
-template <int D> struct Staged {
+template <int D, int STEP> struct Staged {
   static constexpr int kPerRow = D * 2 / 16;
-  static constexpr int kPer = kStep * kPerRow / kThreads;  // chunks per thread
+  static constexpr int kPer = STEP * kPerRow / kThreads;  // chunks per thread
   i32x4 x[kPer];
   __device__ __forceinline__ void fetch(const uint16_t* src, int r0, int N) {
 #pragma unroll
@@ -93,28 +98,30 @@ template <int D> struct Staged {
     for (int c = 0; c < kPer; ++c) {
       const int idx = (int)threadIdx.x + c * kThreads;
       const int row = idx / kPerRow, col = idx - row * kPerRow;
-      *(i32x4*)(lds + row * Geo<D>::kStr + col * 16) = x[c];
+      *(i32x4*)(lds + row * Geo<D, STEP>::kStr + col * 16) = x[c];
     }
   }
 };
 
 // a row of the B operand (16 bytes per 16-element chunk, lane group g holds
 // elements 8g..8g+7 of each chunk)
+template <int D> using RowRegs = i32x4[D / 16];
+template <int D> using TileAcc = f32x16[D / 32];
+
 template <int D>
-__device__ __forceinline__ void load_row(i32x4 (&dst)[Geo<D>::QST], const uint16_t* row, bool ok,
-                                         int g) {
+__device__ __forceinline__ void load_row(RowRegs<D>& dst, const uint16_t* row, bool ok, int g) {
 #pragma unroll
-  for (int t = 0; t < Geo<D>::QST; ++t)
+  for (int t = 0; t < Geo<D, 64>::QST; ++t)
     dst[t] = ok ? *(const i32x4*)(row + 16 * t + 8 * g) : i32x4{0, 0, 0, 0};
 }
 
 // store 32 lanes' transposed accumulators (register r of tile dt: element
 // 32 dt + 8(r/4) + 4g + r%4 of this lane's row), times `mul`, as bf16
 template <int D>
-__device__ __forceinline__ void store_row(uint16_t* dst, const f32x16 (&acc)[Geo<D>::DT],
-                                          float mul, int g) {
+__device__ __forceinline__ void store_row(uint16_t* dst, const TileAcc<D>& acc, float mul,
+                                          int g) {
 #pragma unroll
-  for (int dt = 0; dt < Geo<D>::DT; ++dt)
+  for (int dt = 0; dt < Geo<D, 64>::DT; ++dt)
 #pragma unroll
     for (int b4 = 0; b4 < 4; ++b4) {
       const int d0 = 32 * dt + 8 * b4 + 4 * g;
@@ -129,16 +136,18 @@ __device__ __forceinline__ void store_row(uint16_t* dst, const f32x16 (&acc)[Geo
 
 // lanes' LDS byte offsets: permuted A-operand rows, and the transposing read
 template <int D>
-__device__ __forceinline__ int row_lane(int n) { return perm_row(n) * Geo<D>::kStr; }
+__device__ __forceinline__ int row_lane(int n) { return perm_row(n) * Geo<D, 64>::kStr; }
 template <int D>
 __device__ __forceinline__ int tr_lane(int lane) {
   const int g = lane >> 5;
-  return (8 * g + ((lane & 15) >> 2)) * Geo<D>::kStr + (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
+  return (8 * g + ((lane & 15) >> 2)) * Geo<D, 64>::kStr +
+         (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
 }
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdParams p) {
-  using G = Geo<D>;
+__global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p) {
+  constexpr int kStep = kStepDq;
+  using G = Geo<D, kStep>;
   __shared__ __attribute__((aligned(16))) char smem[2 * G::kBytes];  // K block, V block
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 5, n = lane & 31;
@@ -159,7 +168,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdParams p) {
   const int kend = CAUSAL ? min(N, q0 + kTile) : N;
   const int a_off = row_lane<D>(n) + 16 * g;
   const int t_off = tr_lane<D>(lane);
-  Staged<D> sk, sv;
+  Staged<D, kStep> sk, sv;
   sk.fetch(p.k + hoff, 0, N);
   sv.fetch(p.v + hoff, 0, N);
   for (int kb = 0; kb < kend; kb += kStep) {
@@ -171,9 +180,9 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdParams p) {
       sk.fetch(p.k + hoff, kb + kStep, N);
       sv.fetch(p.v + hoff, kb + kStep, N);
     }
-    f32x16 s[2], dp[2];
+    f32x16 s[kStep / 32], dp[kStep / 32];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+    for (int ks = 0; ks < kStep / 32; ++ks) {
       s[ks] = f32x16{};
       dp[ks] = f32x16{};
       const char* kr = smem + ks * 32 * G::kStr + a_off;
@@ -189,7 +198,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdParams p) {
     // dS^T as the B operand of the next product: keys 16u + 8g + e
     bf16x8 dsb[kStep / 16];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
+    for (int ks = 0; ks < kStep / 32; ++ks)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = kb + 32 * ks + elem_of_reg(r, g);
@@ -212,7 +221,8 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdParams p) {
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads) void bwd_dkv_kernel(BwdParams p) {
-  using G = Geo<D>;
+  constexpr int kStep = kStepDkv;
+  using G = Geo<D, kStep>;
   // Q block, dO block, then the block's lse * log2(e) and delta
   __shared__ __attribute__((aligned(16))) char smem[2 * G::kBytes + 2 * kStep * 4];
   float* lse_t = (float*)(smem + 2 * G::kBytes);
@@ -238,13 +248,15 @@ __global__ __launch_bounds__(kThreads) void bwd_dkv_kernel(BwdParams p) {
   const int t_off = tr_lane<D>(lane);
   // causal: queries below this tile's first key see none of its keys
   const int qstart = CAUSAL ? k0 : 0;
-  Staged<D> sq, sg;
-  float pl = 0.f, pd = 0.f;  // the block's lse * log2(e) and delta (threads < 64)
+  Staged<D, kStep> sq, sg;
+  // the block's lse and delta (threads < 64), raw: any arithmetic on them
+  // here would make the wave wait for every load just issued
+  float pl = 0.f, pd = 0.f;
   auto fetch = [&](int qb) __attribute__((always_inline)) {
     sq.fetch(p.q + hoff, qb, N);
     sg.fetch(p.d_o + hoff, qb, N);
     const int qi = qb + (int)threadIdx.x;
-    pl = threadIdx.x < kStep && qi < N ? p.lse[bh * N + qi] * kLog2e : 0.f;
+    pl = threadIdx.x < kStep && qi < N ? p.lse[bh * N + qi] : 0.f;
     pd = threadIdx.x < kStep && qi < N ? p.delta[bh * N + qi] : 0.f;
   };
   fetch(qstart);
@@ -253,14 +265,14 @@ __global__ __launch_bounds__(kThreads) void bwd_dkv_kernel(BwdParams p) {
     sq.commit(smem);
     sg.commit(smem + G::kBytes);
     if (threadIdx.x < kStep) {
-      lse_t[threadIdx.x] = pl;
+      lse_t[threadIdx.x] = pl * kLog2e;
       dlt_t[threadIdx.x] = pd;
     }
     __syncthreads();
     if (qb + kStep < N) fetch(qb + kStep);
-    f32x16 s[2], dp[2];
+    f32x16 s[kStep / 32], dp[kStep / 32];
 #pragma unroll
-    for (int qs = 0; qs < 2; ++qs) {
+    for (int qs = 0; qs < kStep / 32; ++qs) {
       s[qs] = f32x16{};
       dp[qs] = f32x16{};
       const char* qr = smem + qs * 32 * G::kStr + a_off;
@@ -276,7 +288,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dkv_kernel(BwdParams p) {
     // P and dS as B operands: queries 16u + 8g + e of the block
     bf16x8 pb[kStep / 16], dsb[kStep / 16];
 #pragma unroll
-    for (int qs = 0; qs < 2; ++qs)
+    for (int qs = 0; qs < kStep / 32; ++qs)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int qi = 32 * qs + elem_of_reg(r, g);
