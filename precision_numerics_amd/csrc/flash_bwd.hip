@@ -219,6 +219,131 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p) {
   if (qok) store_row<D>(p.dq + hoff + (int64_t)qrow * D, dq, p.scale, g);
 }
 
+// One query block (kStep = 64 queries, two 32-query subtiles) of the dkv
+// kernel: S = Q K^T and dP = dO V^T for the block's queries against this
+// lane's key, P = exp2(S scale log2(e) - lse log2(e)), dS = P o (dP - delta),
+// then dV^T += dO^T P and dK^T += Q^T dS.  MASK zeroes P of queries past N
+// and (causal) of queries before the key.
+//
+// The block's products form one sequence of slots (S and dP of subtile 0,
+// of subtile 1, then dV and dK of queries 0..15, .., 48..63), placed in
+// program order and fenced against the scheduler.  Each slot issues the LDS
+// reads of the product kAhead slots later, and the softmax arithmetic of a
+// subtile fills the slots that follow its last S and dP product, so that a
+// single wave per SIMD keeps its matrix unit fed.
+template <int I> struct Slot { static constexpr int value = I; };
+
+// f(Slot<0>{}), ..., f(Slot<N-1>{}): a loop whose index is a constant
+template <int N, int I = 0, typename F>
+__device__ __forceinline__ void for_slots(F&& f) {
+  if constexpr (I < N) {
+    f(Slot<I>{});
+    for_slots<N, I + 1>(f);
+  }
+}
+
+template <int D, int kStep, bool CAUSAL, bool MASK>
+__device__ __forceinline__ void dkv_step(const char* smem, const float* lse_t, const float* dlt_t,
+                                         int a_off, int t_off, int g, int qb, int krow, int N,
+                                         float scale_log2, const RowRegs<D>& kv,
+                                         const RowRegs<D>& vv, TileAcc<D>& dk, TileAcc<D>& dv) {
+  static_assert(kStep == 64, "two 32-query subtiles per step");
+  using G = Geo<D, kStep>;
+  constexpr int QST = G::QST, DT = G::DT;
+  constexpr int NM = 2 * QST;           // S and dP products per subtile
+  constexpr int NU = 2 * DT;            // dV and dK products per 16 queries
+  constexpr int NSLOT = 2 * NM + 4 * NU;
+  constexpr int kAhead = 4;
+  constexpr int kSoftRead = 4;          // slots between the lse/delta reads and their use
+  i32x4 qa[2][QST], ga[2][QST];
+  float lv[2][16], dl[2][16];
+  i16x4 tr[4][DT][4];   // per 16 queries and d tile: dO^T lo, hi, Q^T lo, hi
+  f32x16 s[2], dp[2];
+  bf16x8 pb[4], dsb[4];
+
+  auto reads_of = [&](auto mc) __attribute__((always_inline)) {
+    constexpr int m = decltype(mc)::value;
+    if constexpr (m < 2 * NM) {
+      constexpr int qs = m / NM, i = m % NM, t = i >> 1;
+      const char* base = smem + a_off + qs * 32 * G::kStr + 32 * t;
+      if constexpr (i & 1)
+        ga[qs][t] = *(const i32x4*)(base + G::kBytes);
+      else
+        qa[qs][t] = *(const i32x4*)base;
+    } else {
+      constexpr int u = (m - 2 * NM) / NU, i = (m - 2 * NM) % NU, dt = i >> 1;
+      const char* src = smem + ((i & 1) ? 0 : G::kBytes) + t_off + 16 * u * G::kStr + 64 * dt;
+      tr[u][dt][2 * (i & 1)] = lds_read_tr16(src);
+      tr[u][dt][2 * (i & 1) + 1] = lds_read_tr16(src + 4 * G::kStr);
+    }
+  };
+  auto product = [&](auto mc) __attribute__((always_inline)) {
+    constexpr int m = decltype(mc)::value;
+    if constexpr (m < 2 * NM) {
+      constexpr int qs = m / NM, i = m % NM, t = i >> 1;
+      if constexpr (i & 1)
+        dp[qs] = mfma_bf16(__builtin_bit_cast(bf16x8, ga[qs][t]),
+                           __builtin_bit_cast(bf16x8, vv[t]), dp[qs]);
+      else
+        s[qs] = mfma_bf16(__builtin_bit_cast(bf16x8, qa[qs][t]),
+                          __builtin_bit_cast(bf16x8, kv[t]), s[qs]);
+    } else {
+      constexpr int u = (m - 2 * NM) / NU, i = (m - 2 * NM) % NU, dt = i >> 1;
+      if constexpr (i & 1)
+        dk[dt] = mfma_bf16(join_bf16x8(tr[u][dt][2], tr[u][dt][3]), dsb[u], dk[dt]);
+      else
+        dv[dt] = mfma_bf16(join_bf16x8(tr[u][dt][0], tr[u][dt][1]), pb[u], dv[dt]);
+    }
+  };
+  auto read_soft = [&](auto qc) __attribute__((always_inline)) {
+    constexpr int qs = decltype(qc)::value;
+    // lse * log2(e) and delta of queries 32 qs + elem_of_reg(r, g)
+    const float4* l4 = (const float4*)(lse_t + 32 * qs + 8 * g);
+    const float4* d4 = (const float4*)(dlt_t + 32 * qs + 8 * g);
+    for_slots<4>([&](auto hc) __attribute__((always_inline)) {
+      constexpr int h = decltype(hc)::value;
+      const float4 l = l4[(h & 1) + 4 * (h >> 1)], d = d4[(h & 1) + 4 * (h >> 1)];
+      lv[qs][4 * h] = l.x; lv[qs][4 * h + 1] = l.y; lv[qs][4 * h + 2] = l.z; lv[qs][4 * h + 3] = l.w;
+      dl[qs][4 * h] = d.x; dl[qs][4 * h + 1] = d.y; dl[qs][4 * h + 2] = d.z; dl[qs][4 * h + 3] = d.w;
+    });
+  };
+  auto soft = [&](auto qc, auto rc) __attribute__((always_inline)) {
+    constexpr int qs = decltype(qc)::value, r = decltype(rc)::value;
+    float pv = exp2_approx(s[qs][r] * scale_log2 - lv[qs][r]);
+    if constexpr (MASK) {
+      const int qi = qb + 32 * qs + elem_of_reg(r, g);
+      pv = qi < N && (!CAUSAL || krow <= qi) ? pv : 0.f;
+    }
+    pb[2 * qs + (r >> 3)][r & 7] = (__bf16)pv;
+    dsb[2 * qs + (r >> 3)][r & 7] = (__bf16)(pv * (dp[qs][r] - dl[qs][r]));
+  };
+
+  s[0] = s[1] = dp[0] = dp[1] = f32x16{};
+  for_slots<kAhead>([&](auto mc) __attribute__((always_inline)) { reads_of(mc); });
+  __builtin_amdgcn_sched_barrier(0);
+  for_slots<NSLOT>([&](auto mc) __attribute__((always_inline)) {
+    constexpr int m = decltype(mc)::value;
+    product(mc);
+    if constexpr (m + kAhead < NSLOT) reads_of(Slot<m + kAhead>{});
+    if constexpr (m == NM - kSoftRead) read_soft(Slot<0>{});
+    if constexpr (m == 2 * NM - kSoftRead) read_soft(Slot<1>{});
+    if constexpr (m >= NM && m < 2 * NM) {
+      // subtile 0's softmax over subtile 1's products
+      constexpr int E = 16 / NM;
+      for_slots<E>([&](auto ec) __attribute__((always_inline)) {
+        soft(Slot<0>{}, Slot<E * (m - NM) + decltype(ec)::value>{});
+      });
+    } else if constexpr (m >= 2 * NM && m < 2 * NM + 2 * NU) {
+      // subtile 1's softmax over the dV, dK products of queries 0..31
+      constexpr int E = 16 / (2 * NU);
+      for_slots<E>([&](auto ec) __attribute__((always_inline)) {
+        soft(Slot<1>{}, Slot<E * (m - 2 * NM) + decltype(ec)::value>{});
+      });
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  });
+}
+
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads) void bwd_dkv_kernel(BwdParams p) {
   constexpr int kStep = kStepDkv;
@@ -270,44 +395,15 @@ __global__ __launch_bounds__(kThreads) void bwd_dkv_kernel(BwdParams p) {
     }
     __syncthreads();
     if (qb + kStep < N) fetch(qb + kStep);
-    f32x16 s[kStep / 32], dp[kStep / 32];
-#pragma unroll
-    for (int qs = 0; qs < kStep / 32; ++qs) {
-      s[qs] = f32x16{};
-      dp[qs] = f32x16{};
-      const char* qr = smem + qs * 32 * G::kStr + a_off;
-      const char* gr = smem + G::kBytes + qs * 32 * G::kStr + a_off;
-#pragma unroll
-      for (int t = 0; t < G::QST; ++t) {
-        s[qs] = mfma_bf16(__builtin_bit_cast(bf16x8, *(const i32x4*)(qr + 32 * t)),
-                          __builtin_bit_cast(bf16x8, kv[t]), s[qs]);
-        dp[qs] = mfma_bf16(__builtin_bit_cast(bf16x8, *(const i32x4*)(gr + 32 * t)),
-                           __builtin_bit_cast(bf16x8, vv[t]), dp[qs]);
-      }
-    }
-    // P and dS as B operands: queries 16u + 8g + e of the block
-    bf16x8 pb[kStep / 16], dsb[kStep / 16];
-#pragma unroll
-    for (int qs = 0; qs < kStep / 32; ++qs)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int qi = 32 * qs + elem_of_reg(r, g);
-        const bool vis = qb + qi < N && (!CAUSAL || krow <= qb + qi);
-        const float pv = vis ? exp2_approx(s[qs][r] * p.scale_log2 - lse_t[qi]) : 0.f;
-        pb[2 * qs + (r >> 3)][r & 7] = (__bf16)pv;
-        dsb[2 * qs + (r >> 3)][r & 7] = (__bf16)(pv * (dp[qs][r] - dlt_t[qi]));
-      }
-#pragma unroll
-    for (int u = 0; u < kStep / 16; ++u)
-#pragma unroll
-      for (int dt = 0; dt < G::DT; ++dt) {
-        const char* qsrc = smem + t_off + 16 * u * G::kStr + 64 * dt;
-        const char* gsrc = smem + G::kBytes + t_off + 16 * u * G::kStr + 64 * dt;
-        dv[dt] = mfma_bf16(join_bf16x8(lds_read_tr16(gsrc), lds_read_tr16(gsrc + 4 * G::kStr)),
-                           pb[u], dv[dt]);
-        dk[dt] = mfma_bf16(join_bf16x8(lds_read_tr16(qsrc), lds_read_tr16(qsrc + 4 * G::kStr)),
-                           dsb[u], dk[dt]);
-      }
+    // The mask is needed only where the block reaches past N or below this
+    // wave's last key (a wave-uniform test): two copies of the body.
+    const bool full = qb + kStep <= N && (!CAUSAL || k0 + wave * 32 + 31 <= qb);
+    if (full)
+      dkv_step<D, kStep, CAUSAL, false>(smem, lse_t, dlt_t, a_off, t_off, g, qb, krow, N,
+                                        p.scale_log2, kv, vv, dk, dv);
+    else
+      dkv_step<D, kStep, CAUSAL, true>(smem, lse_t, dlt_t, a_off, t_off, g, qb, krow, N,
+                                       p.scale_log2, kv, vv, dk, dv);
   }
   if (kok) {
     store_row<D>(p.dk + hoff + (int64_t)krow * D, dk, p.scale, g);
