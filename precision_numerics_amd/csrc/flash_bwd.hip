@@ -69,8 +69,15 @@ __device__ __forceinline__ int elem_of_reg(int r, int g) { return 16 * (r >> 3) 
 
 template <int D, int STEP> struct Geo {
   static constexpr int kRow = D * 2;         // bf16 row bytes
-  static constexpr int kStr = kRow + 64;     // padded LDS row stride
-  static constexpr int kBytes = STEP * kStr;
+  // Each block sits in LDS twice, with two row paddings: 16 bytes for the
+  // row reads of the A operands (16 lanes read one 16-byte column of 16
+  // rows: the rows then fall on distinct banks) and 64 bytes for the
+  // transposing reads (lanes read 8-byte pieces of four rows, 64 bytes
+  // apart within each row).
+  static constexpr int kStrA = kRow + 16;
+  static constexpr int kStrB = kRow + 64;
+  static constexpr int kBytesA = STEP * kStrA;
+  static constexpr int kBytesB = STEP * kStrB;
   static constexpr int QST = D / 16;         // 16-element chunks of a row
   static constexpr int DT = D / 32;          // 32-row subtiles of a transposed output
 };
@@ -93,12 +100,12 @@ template <int D, int STEP> struct Staged {
                           : i32x4{0, 0, 0, 0};
     }
   }
-  __device__ __forceinline__ void commit(char* lds) const {
+  __device__ __forceinline__ void commit(char* lds, int stride) const {
 #pragma unroll
     for (int c = 0; c < kPer; ++c) {
       const int idx = (int)threadIdx.x + c * kThreads;
       const int row = idx / kPerRow, col = idx - row * kPerRow;
-      *(i32x4*)(lds + row * Geo<D, STEP>::kStr + col * 16) = x[c];
+      *(i32x4*)(lds + row * stride + col * 16) = x[c];
     }
   }
 };
@@ -136,11 +143,11 @@ __device__ __forceinline__ void store_row(uint16_t* dst, const TileAcc<D>& acc, 
 
 // lanes' LDS byte offsets: permuted A-operand rows, and the transposing read
 template <int D>
-__device__ __forceinline__ int row_lane(int n) { return perm_row(n) * Geo<D, 64>::kStr; }
+__device__ __forceinline__ int row_lane(int n) { return perm_row(n) * Geo<D, 64>::kStrA; }
 template <int D>
 __device__ __forceinline__ int tr_lane(int lane) {
   const int g = lane >> 5;
-  return (8 * g + ((lane & 15) >> 2)) * Geo<D, 64>::kStr +
+  return (8 * g + ((lane & 15) >> 2)) * Geo<D, 64>::kStrB +
          (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
 }
 
@@ -148,7 +155,8 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p) {
   constexpr int kStep = kStepDq;
   using G = Geo<D, kStep>;
-  __shared__ __attribute__((aligned(16))) char smem[2 * G::kBytes];  // K block, V block
+  // K and V blocks for the row reads, K again for the transposing reads
+  __shared__ __attribute__((aligned(16))) char smem[2 * G::kBytesA + G::kBytesB];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 5, n = lane & 31;
   const int N = p.n;
@@ -173,8 +181,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p) {
   sv.fetch(p.v + hoff, 0, N);
   for (int kb = 0; kb < kend; kb += kStep) {
     __syncthreads();
-    sk.commit(smem);
-    sv.commit(smem + G::kBytes);
+    sk.commit(smem, G::kStrA);
+    sv.commit(smem + G::kBytesA, G::kStrA);
+    sk.commit(smem + 2 * G::kBytesA, G::kStrB);
     __syncthreads();
     if (kb + kStep < kend) {
       sk.fetch(p.k + hoff, kb + kStep, N);
@@ -185,8 +194,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p) {
     for (int ks = 0; ks < kStep / 32; ++ks) {
       s[ks] = f32x16{};
       dp[ks] = f32x16{};
-      const char* kr = smem + ks * 32 * G::kStr + a_off;
-      const char* vr = smem + G::kBytes + ks * 32 * G::kStr + a_off;
+      const char* kr = smem + ks * 32 * G::kStrA + a_off;
+      const char* vr = smem + G::kBytesA + ks * 32 * G::kStrA + a_off;
 #pragma unroll
       for (int t = 0; t < G::QST; ++t) {
         s[ks] = mfma_bf16(__builtin_bit_cast(bf16x8, *(const i32x4*)(kr + 32 * t)),
@@ -203,16 +212,16 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p) {
       for (int r = 0; r < 16; ++r) {
         const int key = kb + 32 * ks + elem_of_reg(r, g);
         const bool vis = key < N && (!CAUSAL || key <= qrow);
-        const float pv = vis ? exp2_approx(s[ks][r] * p.scale_log2 - lse2) : 0.f;
+        const float pv = vis ? exp2_approx(__builtin_fmaf(s[ks][r], p.scale_log2, -lse2)) : 0.f;
         dsb[2 * ks + (r >> 3)][r & 7] = (__bf16)(pv * (dp[ks][r] - dlt));
       }
 #pragma unroll
     for (int u = 0; u < kStep / 16; ++u)
 #pragma unroll
       for (int dt = 0; dt < G::DT; ++dt) {
-        const char* src = smem + t_off + 16 * u * G::kStr + 64 * dt;
+        const char* src = smem + 2 * G::kBytesA + t_off + 16 * u * G::kStrB + 64 * dt;
         const i16x4 lo = lds_read_tr16(src);
-        const i16x4 hi = lds_read_tr16(src + 4 * G::kStr);
+        const i16x4 hi = lds_read_tr16(src + 4 * G::kStrB);
         dq[dt] = mfma_bf16(join_bf16x8(lo, hi), dsb[u], dq[dt]);
       }
   }
@@ -265,16 +274,17 @@ __device__ __forceinline__ void dkv_step(const char* smem, const float* lse_t, c
     constexpr int m = decltype(mc)::value;
     if constexpr (m < 2 * NM) {
       constexpr int qs = m / NM, i = m % NM, t = i >> 1;
-      const char* base = smem + a_off + qs * 32 * G::kStr + 32 * t;
+      const char* base = smem + a_off + qs * 32 * G::kStrA + 32 * t;
       if constexpr (i & 1)
-        ga[qs][t] = *(const i32x4*)(base + G::kBytes);
+        ga[qs][t] = *(const i32x4*)(base + G::kBytesA);
       else
         qa[qs][t] = *(const i32x4*)base;
     } else {
       constexpr int u = (m - 2 * NM) / NU, i = (m - 2 * NM) % NU, dt = i >> 1;
-      const char* src = smem + ((i & 1) ? 0 : G::kBytes) + t_off + 16 * u * G::kStr + 64 * dt;
+      const char* src = smem + 2 * G::kBytesA + ((i & 1) ? 0 : G::kBytesB) + t_off +
+                        16 * u * G::kStrB + 64 * dt;
       tr[u][dt][2 * (i & 1)] = lds_read_tr16(src);
-      tr[u][dt][2 * (i & 1) + 1] = lds_read_tr16(src + 4 * G::kStr);
+      tr[u][dt][2 * (i & 1) + 1] = lds_read_tr16(src + 4 * G::kStrB);
     }
   };
   auto product = [&](auto mc) __attribute__((always_inline)) {
@@ -309,7 +319,7 @@ __device__ __forceinline__ void dkv_step(const char* smem, const float* lse_t, c
   };
   auto soft = [&](auto qc, auto rc) __attribute__((always_inline)) {
     constexpr int qs = decltype(qc)::value, r = decltype(rc)::value;
-    float pv = exp2_approx(s[qs][r] * scale_log2 - lv[qs][r]);
+    float pv = exp2_approx(__builtin_fmaf(s[qs][r], scale_log2, -lv[qs][r]));
     if constexpr (MASK) {
       const int qi = qb + 32 * qs + elem_of_reg(r, g);
       pv = qi < N && (!CAUSAL || krow <= qi) ? pv : 0.f;
@@ -348,9 +358,10 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads) void bwd_dkv_kernel(BwdParams p) {
   constexpr int kStep = kStepDkv;
   using G = Geo<D, kStep>;
-  // Q block, dO block, then the block's lse * log2(e) and delta
-  __shared__ __attribute__((aligned(16))) char smem[2 * G::kBytes + 2 * kStep * 4];
-  float* lse_t = (float*)(smem + 2 * G::kBytes);
+  // Q and dO blocks for the row reads, again for the transposing reads,
+  // then the block's lse * log2(e) and delta
+  __shared__ __attribute__((aligned(16))) char smem[2 * G::kBytesA + 2 * G::kBytesB + 2 * kStep * 4];
+  float* lse_t = (float*)(smem + 2 * G::kBytesA + 2 * G::kBytesB);
   float* dlt_t = lse_t + kStep;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 5, n = lane & 31;
@@ -384,26 +395,42 @@ __global__ __launch_bounds__(kThreads) void bwd_dkv_kernel(BwdParams p) {
     pl = threadIdx.x < kStep && qi < N ? p.lse[bh * N + qi] : 0.f;
     pd = threadIdx.x < kStep && qi < N ? p.delta[bh * N + qi] : 0.f;
   };
-  fetch(qstart);
-  for (int qb = qstart; qb < N; qb += kStep) {
+  // the block qb into LDS, then the loads of the next block
+  auto stage = [&](int qb) __attribute__((always_inline)) {
     __syncthreads();
-    sq.commit(smem);
-    sg.commit(smem + G::kBytes);
+    sq.commit(smem, G::kStrA);
+    sg.commit(smem + G::kBytesA, G::kStrA);
+    sq.commit(smem + 2 * G::kBytesA, G::kStrB);
+    sg.commit(smem + 2 * G::kBytesA + G::kBytesB, G::kStrB);
     if (threadIdx.x < kStep) {
       lse_t[threadIdx.x] = pl * kLog2e;
       dlt_t[threadIdx.x] = pd;
     }
     __syncthreads();
     if (qb + kStep < N) fetch(qb + kStep);
-    // The mask is needed only where the block reaches past N or below this
-    // wave's last key (a wave-uniform test): two copies of the body.
-    const bool full = qb + kStep <= N && (!CAUSAL || k0 + wave * 32 + 31 <= qb);
-    if (full)
-      dkv_step<D, kStep, CAUSAL, false>(smem, lse_t, dlt_t, a_off, t_off, g, qb, krow, N,
-                                        p.scale_log2, kv, vv, dk, dv);
-    else
-      dkv_step<D, kStep, CAUSAL, true>(smem, lse_t, dlt_t, a_off, t_off, g, qb, krow, N,
-                                       p.scale_log2, kv, vv, dk, dv);
+  };
+  // Blocks that need the mask (causal: the two holding this tile's own
+  // queries; the ragged last block) and the rest run in separate loops, so
+  // that the common one carries no compares and the accumulators keep one
+  // register assignment per loop.
+  const int qfull = CAUSAL ? k0 + kTile : 0;
+  const int nfull = N / kStep * kStep;
+  fetch(qstart);
+  int qb = qstart;
+  for (; qb < min(qfull, N); qb += kStep) {
+    stage(qb);
+    dkv_step<D, kStep, CAUSAL, true>(smem, lse_t, dlt_t, a_off, t_off, g, qb, krow, N,
+                                     p.scale_log2, kv, vv, dk, dv);
+  }
+  for (; qb < nfull; qb += kStep) {
+    stage(qb);
+    dkv_step<D, kStep, CAUSAL, false>(smem, lse_t, dlt_t, a_off, t_off, g, qb, krow, N,
+                                      p.scale_log2, kv, vv, dk, dv);
+  }
+  for (; qb < N; qb += kStep) {
+    stage(qb);
+    dkv_step<D, kStep, CAUSAL, true>(smem, lse_t, dlt_t, a_off, t_off, g, qb, krow, N,
+                                     p.scale_log2, kv, vv, dk, dv);
   }
   if (kok) {
     store_row<D>(p.dk + hoff + (int64_t)krow * D, dk, p.scale, g);

@@ -82,6 +82,33 @@ def test_backward_tiny_shapes(lib, d, causal):
                    f"rel mean {rel[1]:.2e}")
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_d128_many_blocks(lib, causal):
+    """d = 128 over many key and query blocks with a ragged end (N = 1000):
+    the kernels' masked first blocks, unmasked middle blocks and masked last
+    block all run."""
+    import precision_numerics_amd as pna
+    n, d = 1000, 128
+    cfg = synth.small(synth.CONFIGS["c3"], batch=1, heads=2, seq_len=n, head_dim=d,
+                      causal=causal)
+    inp = synth.make_inputs(cfg, seed=77)
+    q, k, v = device_inputs(inp)
+    o, d_o, grads = _grads(pna, q, k, v, causal, seed=7)
+    qf, kf, vf = (x.reshape(2, n, d) for x in oracle_inputs(inp))
+    of = out_to_f64(o).reshape(2, n, d)
+    gf = out_to_f64(d_o).reshape(2, n, d)
+    sc = oracle.default_scale(d)
+    for u in range(2):
+        ref = oracle.attention_backward_head(qf[u], kf[u], vf[u], of[u], gf[u], causal=causal,
+                                             scale=sc)
+        atols = (_atol(d, sc, kf[u], gf[u], vf[u]), _atol(d, sc, qf[u], gf[u], vf[u]), 0.0)
+        for i, name in enumerate(("dq", "dk", "dv")):
+            rel = _check(out_to_f64(grads[i]).reshape(2, n, d)[u], ref[i], f"{name} u={u}",
+                         atols[i])
+            _print(f"backward d=128 n=1000 causal={causal} unit {u} {name}: rel max {rel[0]:.2e} "
+                   f"rel mean {rel[1]:.2e}")
+
+
 def test_backward_workload_shape(lib):
     """The GPT-2-small workload's shape (B8 H12 N1024 d64, causal), sampled
     heads against the oracle, and bitwise reproducible run to run."""
