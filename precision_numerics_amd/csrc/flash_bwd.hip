@@ -151,6 +151,8 @@ __device__ __forceinline__ int tr_lane(int lane) {
          (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
 }
 
+template <bool B> struct Flag { static constexpr bool value = B; };
+
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p) {
   constexpr int kStep = kStepDq;
@@ -177,9 +179,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p) {
   const int a_off = row_lane<D>(n) + 16 * g;
   const int t_off = tr_lane<D>(lane);
   Staged<D, kStep> sk, sv;
-  sk.fetch(p.k + hoff, 0, N);
-  sv.fetch(p.v + hoff, 0, N);
-  for (int kb = 0; kb < kend; kb += kStep) {
+  // the block kb into LDS, then the loads of the next block
+  auto stage = [&](int kb) __attribute__((always_inline)) {
     __syncthreads();
     sk.commit(smem, G::kStrA);
     sv.commit(smem + G::kBytesA, G::kStrA);
@@ -189,6 +190,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p) {
       sk.fetch(p.k + hoff, kb + kStep, N);
       sv.fetch(p.v + hoff, kb + kStep, N);
     }
+  };
+  auto step = [&](int kb, auto maskc) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(maskc)::value;
     f32x16 s[kStep / 32], dp[kStep / 32];
 #pragma unroll
     for (int ks = 0; ks < kStep / 32; ++ks) {
@@ -210,9 +214,11 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p) {
     for (int ks = 0; ks < kStep / 32; ++ks)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int key = kb + 32 * ks + elem_of_reg(r, g);
-        const bool vis = key < N && (!CAUSAL || key <= qrow);
-        const float pv = vis ? exp2_approx(__builtin_fmaf(s[ks][r], p.scale_log2, -lse2)) : 0.f;
+        float pv = exp2_approx(__builtin_fmaf(s[ks][r], p.scale_log2, -lse2));
+        if constexpr (MASK) {
+          const int key = kb + 32 * ks + elem_of_reg(r, g);
+          pv = key < N && (!CAUSAL || key <= qrow) ? pv : 0.f;
+        }
         dsb[2 * ks + (r >> 3)][r & 7] = (__bf16)(pv * (dp[ks][r] - dlt));
       }
 #pragma unroll
@@ -224,6 +230,21 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p) {
         const i16x4 hi = lds_read_tr16(src + 4 * G::kStrB);
         dq[dt] = mfma_bf16(join_bf16x8(lo, hi), dsb[u], dq[dt]);
       }
+  };
+  // Key blocks wholly visible to every query of the tile (causal: below
+  // its first query; all: inside N) run without the mask, the rest (the
+  // tile's diagonal blocks, the ragged last block) with it.
+  const int kfull = min(CAUSAL ? q0 : N, N / kStep * kStep);
+  sk.fetch(p.k + hoff, 0, N);
+  sv.fetch(p.v + hoff, 0, N);
+  int kb = 0;
+  for (; kb < kfull; kb += kStep) {
+    stage(kb);
+    step(kb, Flag<false>{});
+  }
+  for (; kb < kend; kb += kStep) {
+    stage(kb);
+    step(kb, Flag<true>{});
   }
   if (qok) store_row<D>(p.dq + hoff + (int64_t)qrow * D, dq, p.scale, g);
 }
