@@ -44,7 +44,8 @@ HBM_PEAK_GBS = 8000.0
 # the kernel sources it was taken on (sha256 of the files below).
 TRAFFIC_SOURCES = ("precision_numerics_amd/csrc/flash_fwd.hip",
                    "precision_numerics_amd/csrc/device.hpp",
-                   "precision_numerics_amd/csrc/launch.hpp")
+                   "precision_numerics_amd/csrc/launch.hpp",
+                   "precision_numerics_amd/csrc/lds_dma.hpp")
 TRAFFIC = {
     "workload": "c3",
     "sources_sha256": "2caef7d47e60d33024b6cb0ebb18e8f2c3ba7c5c5a7c9627f8cb47fbe73ea4e1",

@@ -26,11 +26,13 @@
 //   dkv kernel: a workgroup owns 128 key rows (a lane per key) and walks the
 //               query blocks: S = Q K^T and dP = dO V^T with permuted query
 //               rows, then dV^T += dO^T P and dK^T += Q^T dS.
-// Tiles of 64 rows are staged in LDS through registers, the next block's
-// global loads overlapping the current block's products (zeros past N);
-// the per-row lse and delta of a query block sit in LDS beside them.
+// The blocks of the other operand stream through two LDS buffers by
+// buffer-to-LDS loads: the loads of block j + 1 run while block j's
+// products do (zeros past N); the per-row lse and delta of a query block
+// sit in LDS beside it.
 #include "device.hpp"
 #include "launch.hpp"
+#include "lds_dma.hpp"
 
 namespace pn {
 namespace {
@@ -76,39 +78,75 @@ template <int D, int STEP> struct Geo {
   // apart within each row).
   static constexpr int kStrA = kRow + 16;
   static constexpr int kStrB = kRow + 64;
-  static constexpr int kBytesA = STEP * kStrA;
-  static constexpr int kBytesB = STEP * kStrB;
+  // 1 KB load segments per copy, and the copy's LDS bytes (whole segments)
+  static constexpr int kSegA = (STEP * kStrA + 1023) / 1024;
+  static constexpr int kSegB = (STEP * kStrB + 1023) / 1024;
+  static constexpr int kBytesA = kSegA * 1024;
+  static constexpr int kBytesB = kSegB * 1024;
   static constexpr int QST = D / 16;         // 16-element chunks of a row
   static constexpr int DT = D / 32;          // 32-row subtiles of a transposed output
 };
 
-// A 64-row block of a [N][D] bf16 matrix moves to LDS in two parts: fetch
-// (16-byte global loads into this thread's registers, zeros past N), issued
-// before the products of the current block so that the loads overlap them,
-// and commit (the registers into the padded LDS tile) after the next
-// barrier.
-template <int D, int STEP> struct Staged {
-  static constexpr int kPerRow = D * 2 / 16;
-  static constexpr int kPer = STEP * kPerRow / kThreads;  // chunks per thread
-  i32x4 x[kPer];
-  __device__ __forceinline__ void fetch(const uint16_t* src, int r0, int N) {
-#pragma unroll
-    for (int c = 0; c < kPer; ++c) {
-      const int idx = (int)threadIdx.x + c * kThreads;
-      const int row = idx / kPerRow, col = idx - row * kPerRow;
-      x[c] = r0 + row < N ? *(const i32x4*)(src + (int64_t)(r0 + row) * D + col * 8)
-                          : i32x4{0, 0, 0, 0};
-    }
+template <int I> struct Slot { static constexpr int value = I; };
+template <bool B> struct Flag { static constexpr bool value = B; };
+
+// f(Slot<0>{}), ..., f(Slot<N-1>{}): a loop whose index is a constant
+template <int N, int I = 0, typename F>
+__device__ __forceinline__ void for_slots(F&& f) {
+  if constexpr (I < N) {
+    f(Slot<I>{});
+    for_slots<N, I + 1>(f);
   }
-  __device__ __forceinline__ void commit(char* lds, int stride) const {
+}
+
+// This wave's share of the buffer-to-LDS loads that fill the two LDS copies
+// of a STEP-row block of a [N][D] bf16 matrix: segments w, w + 4, .. of each
+// copy, with each lane's source offset inside the block (rows past N read
+// zeros through the buffer range check).  Asynchronous: the loads are
+// awaited by an explicit s_waitcnt vmcnt(0) before the barrier that
+// publishes the block.
+template <int D, int STEP> struct BlockDma {
+  using G = Geo<D, STEP>;
+  static constexpr int kPerA = (G::kSegA + 3) / 4;
+  static constexpr int kPerB = (G::kSegB + 3) / 4;
+  uint32_t offA[kPerA], offB[kPerB];
+  int wave;
+  __device__ __forceinline__ void init(int w, int lane) {
+    wave = w;
 #pragma unroll
-    for (int c = 0; c < kPer; ++c) {
-      const int idx = (int)threadIdx.x + c * kThreads;
-      const int row = idx / kPerRow, col = idx - row * kPerRow;
-      *(i32x4*)(lds + row * stride + col * 16) = x[c];
+    for (int i = 0; i < kPerA; ++i) offA[i] = seg_src_offset(w + 4 * i, lane, G::kRow, G::kStrA);
+#pragma unroll
+    for (int i = 0; i < kPerB; ++i) offB[i] = seg_src_offset(w + 4 * i, lane, G::kRow, G::kStrB);
+  }
+  // rows r0.. into the row-read copy at LDS address lds_a and, if B_COPY,
+  // the transposing-read copy at lds_b
+  template <bool B_COPY>
+  __device__ __forceinline__ void issue(i32x4 rs, int r0, uint32_t lds_a, uint32_t lds_b) const {
+    const uint32_t soff = (uint32_t)r0 * G::kRow;
+    for_slots<kPerA>([&](auto ic) __attribute__((always_inline)) {
+      constexpr int i = decltype(ic)::value;
+      if (4 * i + 3 < G::kSegA || wave + 4 * i < G::kSegA)
+        lds_load16<i * 4096>(rs, offA[i], soff, lds_a + wave * 1024);
+    });
+    if constexpr (B_COPY) {
+      for_slots<kPerB>([&](auto ic) __attribute__((always_inline)) {
+        constexpr int i = decltype(ic)::value;
+        if (4 * i + 3 < G::kSegB || wave + 4 * i < G::kSegB)
+          lds_load16<i * 4096>(rs, offB[i], soff, lds_b + wave * 1024);
+      });
     }
   }
 };
+
+__device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Make the row registers' values needed here (the compiler then waits for
+// their loads at this point).
+template <int N>
+__device__ __forceinline__ void settle(i32x4 (&x)[N]) {
+#pragma unroll
+  for (int t = 0; t < N; ++t) asm volatile("" : "+v"(x[t]));
+}
 
 // a row of the B operand (16 bytes per 16-element chunk, lane group g holds
 // elements 8g..8g+7 of each chunk)
@@ -151,14 +189,14 @@ __device__ __forceinline__ int tr_lane(int lane) {
          (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
 }
 
-template <bool B> struct Flag { static constexpr bool value = B; };
-
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p) {
   constexpr int kStep = kStepDq;
   using G = Geo<D, kStep>;
-  // K and V blocks for the row reads, K again for the transposing reads
-  __shared__ __attribute__((aligned(16))) char smem[2 * G::kBytesA + G::kBytesB];
+  // two buffers, each: K and V blocks for the row reads, K again for the
+  // transposing reads
+  constexpr int kBuf = 2 * G::kBytesA + G::kBytesB;
+  __shared__ __attribute__((aligned(16))) char smem[2 * kBuf];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 5, n = lane & 31;
   const int N = p.n;
@@ -170,36 +208,46 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p) {
   i32x4 qv[G::QST], gv[G::QST];
   load_row<D>(qv, p.q + hoff + (int64_t)qrow * D, qok, g);
   load_row<D>(gv, p.d_o + hoff + (int64_t)qrow * D, qok, g);
-  const float lse2 = qok ? p.lse[bh * N + qrow] * kLog2e : 0.f;
-  const float dlt = qok ? p.delta[bh * N + qrow] : 0.f;
+  float lse2 = qok ? p.lse[bh * N + qrow] * kLog2e : 0.f;
+  float dlt = qok ? p.delta[bh * N + qrow] : 0.f;
+  // The loop's loads are not visible to the compiler's wait counting: its
+  // wait for these values must fall here, not inside the loop, where it
+  // would also wait for the next block's loads.
+  settle(qv);
+  settle(gv);
+  asm volatile("" : "+v"(lse2), "+v"(dlt));
   f32x16 dq[G::DT];
 #pragma unroll
   for (int dt = 0; dt < G::DT; ++dt) dq[dt] = f32x16{};
   const int kend = CAUSAL ? min(N, q0 + kTile) : N;
   const int a_off = row_lane<D>(n) + 16 * g;
   const int t_off = tr_lane<D>(lane);
-  Staged<D, kStep> sk, sv;
-  // the block kb into LDS, then the loads of the next block
-  auto stage = [&](int kb) __attribute__((always_inline)) {
-    __syncthreads();
-    sk.commit(smem, G::kStrA);
-    sv.commit(smem + G::kBytesA, G::kStrA);
-    sk.commit(smem + 2 * G::kBytesA, G::kStrB);
-    __syncthreads();
-    if (kb + kStep < kend) {
-      sk.fetch(p.k + hoff, kb + kStep, N);
-      sv.fetch(p.v + hoff, kb + kStep, N);
-    }
+  BlockDma<D, kStep> dma;
+  dma.init(__builtin_amdgcn_readfirstlane(wave), lane);
+  const i32x4 rsK = buffer_rsrc(p.k + hoff, (uint32_t)N * G::kRow);
+  const i32x4 rsV = buffer_rsrc(p.v + hoff, (uint32_t)N * G::kRow);
+  auto issue = [&](int kb, int buf) __attribute__((always_inline)) {
+    const uint32_t b = lds_address(smem) + buf * kBuf;
+    dma.template issue<true>(rsK, kb, b, b + 2 * G::kBytesA);
+    dma.template issue<false>(rsV, kb, b + G::kBytesA, 0);
   };
-  auto step = [&](int kb, auto maskc) __attribute__((always_inline)) {
+  // block kb (in buffer buf) complete and visible; then the next block's
+  // loads into the other buffer, whose last reader was the previous step
+  auto stage = [&](int kb, int buf) __attribute__((always_inline)) {
+    wait_loads();
+    __syncthreads();
+    if (kb + kStep < kend) issue(kb + kStep, buf ^ 1);
+  };
+  auto step = [&](int kb, int buf, auto maskc) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(maskc)::value;
+    const char* smem_b = smem + buf * kBuf;
     f32x16 s[kStep / 32], dp[kStep / 32];
 #pragma unroll
     for (int ks = 0; ks < kStep / 32; ++ks) {
       s[ks] = f32x16{};
       dp[ks] = f32x16{};
-      const char* kr = smem + ks * 32 * G::kStrA + a_off;
-      const char* vr = smem + G::kBytesA + ks * 32 * G::kStrA + a_off;
+      const char* kr = smem_b + ks * 32 * G::kStrA + a_off;
+      const char* vr = smem_b + G::kBytesA + ks * 32 * G::kStrA + a_off;
 #pragma unroll
       for (int t = 0; t < G::QST; ++t) {
         s[ks] = mfma_bf16(__builtin_bit_cast(bf16x8, *(const i32x4*)(kr + 32 * t)),
@@ -225,7 +273,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p) {
     for (int u = 0; u < kStep / 16; ++u)
 #pragma unroll
       for (int dt = 0; dt < G::DT; ++dt) {
-        const char* src = smem + 2 * G::kBytesA + t_off + 16 * u * G::kStrB + 64 * dt;
+        const char* src = smem_b + 2 * G::kBytesA + t_off + 16 * u * G::kStrB + 64 * dt;
         const i16x4 lo = lds_read_tr16(src);
         const i16x4 hi = lds_read_tr16(src + 4 * G::kStrB);
         dq[dt] = mfma_bf16(join_bf16x8(lo, hi), dsb[u], dq[dt]);
@@ -235,16 +283,15 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p) {
   // its first query; all: inside N) run without the mask, the rest (the
   // tile's diagonal blocks, the ragged last block) with it.
   const int kfull = min(CAUSAL ? q0 : N, N / kStep * kStep);
-  sk.fetch(p.k + hoff, 0, N);
-  sv.fetch(p.v + hoff, 0, N);
-  int kb = 0;
-  for (; kb < kfull; kb += kStep) {
-    stage(kb);
-    step(kb, Flag<false>{});
+  issue(0, 0);
+  int kb = 0, buf = 0;
+  for (; kb < kfull; kb += kStep, buf ^= 1) {
+    stage(kb, buf);
+    step(kb, buf, Flag<false>{});
   }
-  for (; kb < kend; kb += kStep) {
-    stage(kb);
-    step(kb, Flag<true>{});
+  for (; kb < kend; kb += kStep, buf ^= 1) {
+    stage(kb, buf);
+    step(kb, buf, Flag<true>{});
   }
   if (qok) store_row<D>(p.dq + hoff + (int64_t)qrow * D, dq, p.scale, g);
 }
@@ -261,17 +308,6 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p) {
 // reads of the product kAhead slots later, and the softmax arithmetic of a
 // subtile fills the slots that follow its last S and dP product, so that a
 // single wave per SIMD keeps its matrix unit fed.
-template <int I> struct Slot { static constexpr int value = I; };
-
-// f(Slot<0>{}), ..., f(Slot<N-1>{}): a loop whose index is a constant
-template <int N, int I = 0, typename F>
-__device__ __forceinline__ void for_slots(F&& f) {
-  if constexpr (I < N) {
-    f(Slot<I>{});
-    for_slots<N, I + 1>(f);
-  }
-}
-
 template <int D, int kStep, bool CAUSAL, bool MASK>
 __device__ __forceinline__ void dkv_step(const char* smem, const float* lse_t, const float* dlt_t,
                                          int a_off, int t_off, int g, int qb, int krow, int N,
@@ -328,19 +364,22 @@ __device__ __forceinline__ void dkv_step(const char* smem, const float* lse_t, c
   };
   auto read_soft = [&](auto qc) __attribute__((always_inline)) {
     constexpr int qs = decltype(qc)::value;
-    // lse * log2(e) and delta of queries 32 qs + elem_of_reg(r, g)
+    // -lse log2(e) and delta of queries 32 qs + elem_of_reg(r, g)
     const float4* l4 = (const float4*)(lse_t + 32 * qs + 8 * g);
     const float4* d4 = (const float4*)(dlt_t + 32 * qs + 8 * g);
     for_slots<4>([&](auto hc) __attribute__((always_inline)) {
       constexpr int h = decltype(hc)::value;
       const float4 l = l4[(h & 1) + 4 * (h >> 1)], d = d4[(h & 1) + 4 * (h >> 1)];
-      lv[qs][4 * h] = l.x; lv[qs][4 * h + 1] = l.y; lv[qs][4 * h + 2] = l.z; lv[qs][4 * h + 3] = l.w;
+      lv[qs][4 * h] = -kLog2e * l.x;
+      lv[qs][4 * h + 1] = -kLog2e * l.y;
+      lv[qs][4 * h + 2] = -kLog2e * l.z;
+      lv[qs][4 * h + 3] = -kLog2e * l.w;
       dl[qs][4 * h] = d.x; dl[qs][4 * h + 1] = d.y; dl[qs][4 * h + 2] = d.z; dl[qs][4 * h + 3] = d.w;
     });
   };
   auto soft = [&](auto qc, auto rc) __attribute__((always_inline)) {
     constexpr int qs = decltype(qc)::value, r = decltype(rc)::value;
-    float pv = exp2_approx(__builtin_fmaf(s[qs][r], scale_log2, -lv[qs][r]));
+    float pv = exp2_approx(__builtin_fmaf(s[qs][r], scale_log2, lv[qs][r]));
     if constexpr (MASK) {
       const int qi = qb + 32 * qs + elem_of_reg(r, g);
       pv = qi < N && (!CAUSAL || krow <= qi) ? pv : 0.f;
@@ -379,11 +418,11 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads) void bwd_dkv_kernel(BwdParams p) {
   constexpr int kStep = kStepDkv;
   using G = Geo<D, kStep>;
-  // Q and dO blocks for the row reads, again for the transposing reads,
-  // then the block's lse * log2(e) and delta
-  __shared__ __attribute__((aligned(16))) char smem[2 * G::kBytesA + 2 * G::kBytesB + 2 * kStep * 4];
-  float* lse_t = (float*)(smem + 2 * G::kBytesA + 2 * G::kBytesB);
-  float* dlt_t = lse_t + kStep;
+  // two buffers, each: Q and dO blocks for the row reads, again for the
+  // transposing reads, then the block's lse and delta
+  constexpr int kOffL = 2 * G::kBytesA + 2 * G::kBytesB;
+  constexpr int kBuf = kOffL + 2 * kStep * 4;
+  __shared__ __attribute__((aligned(16))) char smem[2 * kBuf];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 5, n = lane & 31;
   const int N = p.n;
@@ -395,6 +434,11 @@ __global__ __launch_bounds__(kThreads) void bwd_dkv_kernel(BwdParams p) {
   i32x4 kv[G::QST], vv[G::QST];
   load_row<D>(kv, p.k + hoff + (int64_t)krow * D, kok, g);
   load_row<D>(vv, p.v + hoff + (int64_t)krow * D, kok, g);
+  // The loop's loads are not visible to the compiler's wait counting: its
+  // wait for these rows must fall here, not inside the loop, where it would
+  // also wait for the next block's loads.
+  settle(kv);
+  settle(vv);
   f32x16 dk[G::DT], dv[G::DT];
 #pragma unroll
   for (int dt = 0; dt < G::DT; ++dt) {
@@ -405,30 +449,33 @@ __global__ __launch_bounds__(kThreads) void bwd_dkv_kernel(BwdParams p) {
   const int t_off = tr_lane<D>(lane);
   // causal: queries below this tile's first key see none of its keys
   const int qstart = CAUSAL ? k0 : 0;
-  Staged<D, kStep> sq, sg;
-  // the block's lse and delta (threads < 64), raw: any arithmetic on them
-  // here would make the wave wait for every load just issued
-  float pl = 0.f, pd = 0.f;
-  auto fetch = [&](int qb) __attribute__((always_inline)) {
-    sq.fetch(p.q + hoff, qb, N);
-    sg.fetch(p.d_o + hoff, qb, N);
-    const int qi = qb + (int)threadIdx.x;
-    pl = threadIdx.x < kStep && qi < N ? p.lse[bh * N + qi] : 0.f;
-    pd = threadIdx.x < kStep && qi < N ? p.delta[bh * N + qi] : 0.f;
+  BlockDma<D, kStep> dma;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  dma.init(wv, lane);
+  const i32x4 rsQ = buffer_rsrc(p.q + hoff, (uint32_t)N * G::kRow);
+  const i32x4 rsG = buffer_rsrc(p.d_o + hoff, (uint32_t)N * G::kRow);
+  const i32x4 rsL = buffer_rsrc(p.lse + bh * N, (uint32_t)N * 4);
+  const i32x4 rsD = buffer_rsrc(p.delta + bh * N, (uint32_t)N * 4);
+  static_assert(kStep == 64, "one 4-byte load per lane fills a block's lse or delta");
+  auto issue = [&](int qb, int buf) __attribute__((always_inline)) {
+    const uint32_t b = lds_address(smem) + buf * kBuf;
+    dma.template issue<true>(rsQ, qb, b, b + 2 * G::kBytesA);
+    dma.template issue<true>(rsG, qb, b + G::kBytesA, b + 2 * G::kBytesA + G::kBytesB);
+    if (wv == 0) lds_load4(rsL, (uint32_t)lane * 4, (uint32_t)qb * 4, b + kOffL);
+    if (wv == 1) lds_load4(rsD, (uint32_t)lane * 4, (uint32_t)qb * 4, b + kOffL + kStep * 4);
   };
-  // the block qb into LDS, then the loads of the next block
-  auto stage = [&](int qb) __attribute__((always_inline)) {
+  // block qb (in buffer buf) complete and visible; then the next block's
+  // loads into the other buffer, whose last reader was the previous step
+  auto stage = [&](int qb, int buf) __attribute__((always_inline)) {
+    wait_loads();
     __syncthreads();
-    sq.commit(smem, G::kStrA);
-    sg.commit(smem + G::kBytesA, G::kStrA);
-    sq.commit(smem + 2 * G::kBytesA, G::kStrB);
-    sg.commit(smem + 2 * G::kBytesA + G::kBytesB, G::kStrB);
-    if (threadIdx.x < kStep) {
-      lse_t[threadIdx.x] = pl * kLog2e;
-      dlt_t[threadIdx.x] = pd;
-    }
-    __syncthreads();
-    if (qb + kStep < N) fetch(qb + kStep);
+    if (qb + kStep < N) issue(qb + kStep, buf ^ 1);
+  };
+  auto run = [&](int qb, int buf, auto maskc) __attribute__((always_inline)) {
+    const char* b = smem + buf * kBuf;
+    dkv_step<D, kStep, CAUSAL, decltype(maskc)::value>(
+        b, (const float*)(b + kOffL), (const float*)(b + kOffL + kStep * 4), a_off, t_off, g, qb,
+        krow, N, p.scale_log2, kv, vv, dk, dv);
   };
   // Blocks that need the mask (causal: the two holding this tile's own
   // queries; the ragged last block) and the rest run in separate loops, so
@@ -436,22 +483,19 @@ __global__ __launch_bounds__(kThreads) void bwd_dkv_kernel(BwdParams p) {
   // register assignment per loop.
   const int qfull = CAUSAL ? k0 + kTile : 0;
   const int nfull = N / kStep * kStep;
-  fetch(qstart);
-  int qb = qstart;
-  for (; qb < min(qfull, N); qb += kStep) {
-    stage(qb);
-    dkv_step<D, kStep, CAUSAL, true>(smem, lse_t, dlt_t, a_off, t_off, g, qb, krow, N,
-                                     p.scale_log2, kv, vv, dk, dv);
+  issue(qstart, 0);
+  int qb = qstart, buf = 0;
+  for (; qb < min(qfull, N); qb += kStep, buf ^= 1) {
+    stage(qb, buf);
+    run(qb, buf, Flag<true>{});
   }
-  for (; qb < nfull; qb += kStep) {
-    stage(qb);
-    dkv_step<D, kStep, CAUSAL, false>(smem, lse_t, dlt_t, a_off, t_off, g, qb, krow, N,
-                                      p.scale_log2, kv, vv, dk, dv);
+  for (; qb < nfull; qb += kStep, buf ^= 1) {
+    stage(qb, buf);
+    run(qb, buf, Flag<false>{});
   }
-  for (; qb < N; qb += kStep) {
-    stage(qb);
-    dkv_step<D, kStep, CAUSAL, true>(smem, lse_t, dlt_t, a_off, t_off, g, qb, krow, N,
-                                     p.scale_log2, kv, vv, dk, dv);
+  for (; qb < N; qb += kStep, buf ^= 1) {
+    stage(qb, buf);
+    run(qb, buf, Flag<true>{});
   }
   if (kok) {
     store_row<D>(p.dk + hoff + (int64_t)krow * D, dk, p.scale, g);
