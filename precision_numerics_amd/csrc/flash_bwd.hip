@@ -58,6 +58,7 @@ struct BwdParams {
   uint16_t* dv;
   int n;
   int tiles;          // 128-row tiles per head
+  int bh_count;       // batch * heads
   float scale;
   float scale_log2;   // scale * log2(e)
 };
@@ -68,6 +69,25 @@ __device__ __forceinline__ int perm_row(int m) {
   return 16 * (m >> 4) + 8 * ((m >> 2) & 1) + 4 * ((m >> 3) & 1) + (m & 3);
 }
 __device__ __forceinline__ int elem_of_reg(int r, int g) { return 16 * (r >> 3) + 8 * g + (r & 7); }
+
+// Workgroup -> (head, tile).  Causal tiles differ in length (the dkv
+// kernel's tile t walks N - 128 t queries, the dq kernel's 128 (t + 1)
+// keys), so they go out longest first, every head's tile of one length
+// together: the short ones then fill the machine at the end instead of a
+// few long ones running alone.  Without the mask all tiles are equal and
+// a head's tiles go out together.
+template <bool CAUSAL, bool LONG_FIRST_LOW>
+__device__ __forceinline__ void tile_of(const BwdParams& p, int64_t& bh, int& tile) {
+  const int64_t b = blockIdx.x;
+  if constexpr (CAUSAL) {
+    const int t = (int)(b / p.bh_count);
+    bh = b - (int64_t)t * p.bh_count;
+    tile = LONG_FIRST_LOW ? t : p.tiles - 1 - t;
+  } else {
+    bh = b / p.tiles;
+    tile = (int)(b - bh * p.tiles);
+  }
+}
 
 template <int D, int STEP> struct Geo {
   static constexpr int kRow = D * 2;         // bf16 row bytes
@@ -200,8 +220,10 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 5, n = lane & 31;
   const int N = p.n;
-  const int64_t bh = blockIdx.x / p.tiles;
-  const int q0 = (int)(blockIdx.x - bh * p.tiles) * kTile;
+  int64_t bh;
+  int tile;
+  tile_of<CAUSAL, false>(p, bh, tile);
+  const int q0 = tile * kTile;
   const int qrow = q0 + wave * 32 + n;
   const bool qok = qrow < N;
   const int64_t hoff = bh * (int64_t)N * D;
@@ -426,8 +448,10 @@ __global__ __launch_bounds__(kThreads) void bwd_dkv_kernel(BwdParams p) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 5, n = lane & 31;
   const int N = p.n;
-  const int64_t bh = blockIdx.x / p.tiles;
-  const int k0 = (int)(blockIdx.x - bh * p.tiles) * kTile;
+  int64_t bh;
+  int tile;
+  tile_of<CAUSAL, true>(p, bh, tile);
+  const int k0 = tile * kTile;
   const int krow = k0 + wave * 32 + n;
   const bool kok = krow < N;
   const int64_t hoff = bh * (int64_t)N * D;
@@ -532,6 +556,7 @@ hipError_t launch_flash_bwd(const AttnBwdArgs& a, hipStream_t st) {
   bp.dv = (uint16_t*)a.dv;
   bp.n = (int)a.seq_len;
   bp.tiles = (int)((a.seq_len + kTile - 1) / kTile);
+  bp.bh_count = (int)bh;
   bp.scale = a.scale;
   bp.scale_log2 = (float)((double)a.scale * 1.4426950408889634);
   if (a.head_dim == 64)
