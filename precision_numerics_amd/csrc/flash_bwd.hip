@@ -39,12 +39,10 @@ namespace {
 
 constexpr int kThreads = 256;   // four waves
 constexpr int kTile = 128;      // rows a workgroup owns (32 per wave)
-// Rows of the other operand per step: 32 for the dq kernel, whose registers
-// then fit two workgroups per compute unit (two waves per SIMD, one
-// covering the other's latencies), 64 for the dkv kernel, whose two output
-// accumulators keep it at one wave per SIMD anyway.
+// Rows of the other operand per step (both kernels run two waves per SIMD,
+// one covering the other's latencies).
 constexpr int kStepDq = 32;
-constexpr int kStepDkv = 64;
+constexpr int kStepDkv = 32;
 
 struct BwdParams {
   const uint16_t* q;
@@ -70,23 +68,30 @@ __device__ __forceinline__ int perm_row(int m) {
 }
 __device__ __forceinline__ int elem_of_reg(int r, int g) { return 16 * (r >> 3) + 8 * g + (r & 7); }
 
-// Workgroup -> (head, tile).  Causal tiles differ in length (the dkv
-// kernel's tile t walks N - 128 t queries, the dq kernel's 128 (t + 1)
-// keys), so they go out longest first, every head's tile of one length
-// together: the short ones then fill the machine at the end instead of a
-// few long ones running alone.  Without the mask all tiles are equal and
-// a head's tiles go out together.
+// Workgroup -> (head, tile).  Workgroups go to the eight XCDs in turn, so
+// heads are taken in groups of eight, head 8c + x on XCD x: each XCD then
+// works through its heads one at a time, all tiles of a head together, and
+// the head's K, V, Q, dO rows stay in that XCD's L2.  Within a head,
+// causal tiles differ in length (the dkv kernel's tile t walks N - 128 t
+// queries, the dq kernel's 128 (t + 1) keys) and go out longest first, so
+// short ones fill the machine at the end.  Heads past the last whole group
+// of eight follow one after another.
 template <bool CAUSAL, bool LONG_FIRST_LOW>
 __device__ __forceinline__ void tile_of(const BwdParams& p, int64_t& bh, int& tile) {
   const int64_t b = blockIdx.x;
-  if constexpr (CAUSAL) {
-    const int t = (int)(b / p.bh_count);
-    bh = b - (int64_t)t * p.bh_count;
-    tile = LONG_FIRST_LOW ? t : p.tiles - 1 - t;
+  const int T = p.tiles;
+  const int64_t grouped = (int64_t)(p.bh_count / 8) * 8 * T;
+  int t;
+  if (b < grouped) {
+    const int64_t m = b >> 3;
+    bh = (m / T) * 8 + (b & 7);
+    t = (int)(m % T);
   } else {
-    bh = b / p.tiles;
-    tile = (int)(b - bh * p.tiles);
+    const int64_t r = b - grouped;
+    bh = (int64_t)(p.bh_count / 8) * 8 + r / T;
+    t = (int)(r % T);
   }
+  tile = !CAUSAL || LONG_FIRST_LOW ? t : T - 1 - t;
 }
 
 template <int D, int STEP> struct Geo {
@@ -120,23 +125,23 @@ __device__ __forceinline__ void for_slots(F&& f) {
 }
 
 // This wave's share of the buffer-to-LDS loads that fill the two LDS copies
-// of a STEP-row block of a [N][D] bf16 matrix: segments w, w + 4, .. of each
-// copy, with each lane's source offset inside the block (rows past N read
-// zeros through the buffer range check).  Asynchronous: the loads are
-// awaited by an explicit s_waitcnt vmcnt(0) before the barrier that
-// publishes the block.
-template <int D, int STEP> struct BlockDma {
+// of a STEP-row block of a [N][D] bf16 matrix, among W issuing waves:
+// segments w, w + W, .. of each copy, with each lane's source offset inside
+// the block (rows past N read zeros through the buffer range check).
+// Asynchronous: the loads are awaited by an explicit s_waitcnt vmcnt(0)
+// before the barrier that publishes the block.
+template <int D, int STEP, int W> struct BlockDma {
   using G = Geo<D, STEP>;
-  static constexpr int kPerA = (G::kSegA + 3) / 4;
-  static constexpr int kPerB = (G::kSegB + 3) / 4;
+  static constexpr int kPerA = (G::kSegA + W - 1) / W;
+  static constexpr int kPerB = (G::kSegB + W - 1) / W;
   uint32_t offA[kPerA], offB[kPerB];
   int wave;
   __device__ __forceinline__ void init(int w, int lane) {
     wave = w;
 #pragma unroll
-    for (int i = 0; i < kPerA; ++i) offA[i] = seg_src_offset(w + 4 * i, lane, G::kRow, G::kStrA);
+    for (int i = 0; i < kPerA; ++i) offA[i] = seg_src_offset(w + W * i, lane, G::kRow, G::kStrA);
 #pragma unroll
-    for (int i = 0; i < kPerB; ++i) offB[i] = seg_src_offset(w + 4 * i, lane, G::kRow, G::kStrB);
+    for (int i = 0; i < kPerB; ++i) offB[i] = seg_src_offset(w + W * i, lane, G::kRow, G::kStrB);
   }
   // rows r0.. into the row-read copy at LDS address lds_a and, if B_COPY,
   // the transposing-read copy at lds_b
@@ -145,14 +150,14 @@ template <int D, int STEP> struct BlockDma {
     const uint32_t soff = (uint32_t)r0 * G::kRow;
     for_slots<kPerA>([&](auto ic) __attribute__((always_inline)) {
       constexpr int i = decltype(ic)::value;
-      if (4 * i + 3 < G::kSegA || wave + 4 * i < G::kSegA)
-        lds_load16<i * 4096>(rs, offA[i], soff, lds_a + wave * 1024);
+      if (W * i + W - 1 < G::kSegA || wave + W * i < G::kSegA)
+        lds_load16<i * W * 1024>(rs, offA[i], soff, lds_a + wave * 1024);
     });
     if constexpr (B_COPY) {
       for_slots<kPerB>([&](auto ic) __attribute__((always_inline)) {
         constexpr int i = decltype(ic)::value;
-        if (4 * i + 3 < G::kSegB || wave + 4 * i < G::kSegB)
-          lds_load16<i * 4096>(rs, offB[i], soff, lds_b + wave * 1024);
+        if (W * i + W - 1 < G::kSegB || wave + W * i < G::kSegB)
+          lds_load16<i * W * 1024>(rs, offB[i], soff, lds_b + wave * 1024);
       });
     }
   }
@@ -244,10 +249,11 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p) {
   const int kend = CAUSAL ? min(N, q0 + kTile) : N;
   const int a_off = row_lane<D>(n) + 16 * g;
   const int t_off = tr_lane<D>(lane);
-  BlockDma<D, kStep> dma;
+  BlockDma<D, kStep, 4> dma;
   dma.init(__builtin_amdgcn_readfirstlane(wave), lane);
-  const i32x4 rsK = buffer_rsrc(p.k + hoff, (uint32_t)N * G::kRow);
-  const i32x4 rsV = buffer_rsrc(p.v + hoff, (uint32_t)N * G::kRow);
+  // the descriptors are uniform: made scalar once here, not at every load
+  const i32x4 rsK = uniform(buffer_rsrc(p.k + hoff, (uint32_t)N * G::kRow));
+  const i32x4 rsV = uniform(buffer_rsrc(p.v + hoff, (uint32_t)N * G::kRow));
   auto issue = [&](int kb, int buf) __attribute__((always_inline)) {
     const uint32_t b = lds_address(smem) + buf * kBuf;
     dma.template issue<true>(rsK, kb, b, b + 2 * G::kBytesA);
@@ -318,219 +324,206 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p) {
   if (qok) store_row<D>(p.dq + hoff + (int64_t)qrow * D, dq, p.scale, g);
 }
 
-// One query block (kStep = 64 queries, two 32-query subtiles) of the dkv
-// kernel: S = Q K^T and dP = dO V^T for the block's queries against this
-// lane's key, P = exp2(S scale log2(e) - lse log2(e)), dS = P o (dP - delta),
-// then dV^T += dO^T P and dK^T += Q^T dS.  MASK zeroes P of queries past N
-// and (causal) of queries before the key.
-//
-// The block's products form one sequence of slots (S and dP of subtile 0,
-// of subtile 1, then dV and dK of queries 0..15, .., 48..63), placed in
-// program order and fenced against the scheduler.  Each slot issues the LDS
-// reads of the product kAhead slots later, and the softmax arithmetic of a
-// subtile fills the slots that follow its last S and dP product, so that a
-// single wave per SIMD keeps its matrix unit fed.
-template <int D, int kStep, bool CAUSAL, bool MASK>
-__device__ __forceinline__ void dkv_step(const char* smem, const float* lse_t, const float* dlt_t,
-                                         int a_off, int t_off, int g, int qb, int krow, int N,
-                                         float scale_log2, const RowRegs<D>& kv,
-                                         const RowRegs<D>& vv, TileAcc<D>& dk, TileAcc<D>& dv) {
-  static_assert(kStep == 64, "two 32-query subtiles per step");
-  using G = Geo<D, kStep>;
-  constexpr int QST = G::QST, DT = G::DT;
-  constexpr int NM = 2 * QST;           // S and dP products per subtile
-  constexpr int NU = 2 * DT;            // dV and dK products per 16 queries
-  constexpr int NSLOT = 2 * NM + 4 * NU;
-  constexpr int kAhead = 4;
-  constexpr int kSoftRead = 4;          // slots between the lse/delta reads and their use
-  i32x4 qa[2][QST], ga[2][QST];
-  float lv[2][16], dl[2][16];
-  i16x4 tr[4][DT][4];   // per 16 queries and d tile: dO^T lo, hi, Q^T lo, hi
-  f32x16 s[2], dp[2];
-  bf16x8 pb[4], dsb[4];
-
-  auto reads_of = [&](auto mc) __attribute__((always_inline)) {
-    constexpr int m = decltype(mc)::value;
-    if constexpr (m < 2 * NM) {
-      constexpr int qs = m / NM, i = m % NM, t = i >> 1;
-      const char* base = smem + a_off + qs * 32 * G::kStrA + 32 * t;
-      if constexpr (i & 1)
-        ga[qs][t] = *(const i32x4*)(base + G::kBytesA);
-      else
-        qa[qs][t] = *(const i32x4*)base;
-    } else {
-      constexpr int u = (m - 2 * NM) / NU, i = (m - 2 * NM) % NU, dt = i >> 1;
-      const char* src = smem + 2 * G::kBytesA + ((i & 1) ? 0 : G::kBytesB) + t_off +
-                        16 * u * G::kStrB + 64 * dt;
-      tr[u][dt][2 * (i & 1)] = lds_read_tr16(src);
-      tr[u][dt][2 * (i & 1) + 1] = lds_read_tr16(src + 4 * G::kStrB);
-    }
-  };
-  auto product = [&](auto mc) __attribute__((always_inline)) {
-    constexpr int m = decltype(mc)::value;
-    if constexpr (m < 2 * NM) {
-      constexpr int qs = m / NM, i = m % NM, t = i >> 1;
-      if constexpr (i & 1)
-        dp[qs] = mfma_bf16(__builtin_bit_cast(bf16x8, ga[qs][t]),
-                           __builtin_bit_cast(bf16x8, vv[t]), dp[qs]);
-      else
-        s[qs] = mfma_bf16(__builtin_bit_cast(bf16x8, qa[qs][t]),
-                          __builtin_bit_cast(bf16x8, kv[t]), s[qs]);
-    } else {
-      constexpr int u = (m - 2 * NM) / NU, i = (m - 2 * NM) % NU, dt = i >> 1;
-      if constexpr (i & 1)
-        dk[dt] = mfma_bf16(join_bf16x8(tr[u][dt][2], tr[u][dt][3]), dsb[u], dk[dt]);
-      else
-        dv[dt] = mfma_bf16(join_bf16x8(tr[u][dt][0], tr[u][dt][1]), pb[u], dv[dt]);
-    }
-  };
-  auto read_soft = [&](auto qc) __attribute__((always_inline)) {
-    constexpr int qs = decltype(qc)::value;
-    // -lse log2(e) and delta of queries 32 qs + elem_of_reg(r, g)
-    const float4* l4 = (const float4*)(lse_t + 32 * qs + 8 * g);
-    const float4* d4 = (const float4*)(dlt_t + 32 * qs + 8 * g);
-    for_slots<4>([&](auto hc) __attribute__((always_inline)) {
-      constexpr int h = decltype(hc)::value;
-      const float4 l = l4[(h & 1) + 4 * (h >> 1)], d = d4[(h & 1) + 4 * (h >> 1)];
-      lv[qs][4 * h] = -kLog2e * l.x;
-      lv[qs][4 * h + 1] = -kLog2e * l.y;
-      lv[qs][4 * h + 2] = -kLog2e * l.z;
-      lv[qs][4 * h + 3] = -kLog2e * l.w;
-      dl[qs][4 * h] = d.x; dl[qs][4 * h + 1] = d.y; dl[qs][4 * h + 2] = d.z; dl[qs][4 * h + 3] = d.w;
-    });
-  };
-  auto soft = [&](auto qc, auto rc) __attribute__((always_inline)) {
-    constexpr int qs = decltype(qc)::value, r = decltype(rc)::value;
-    float pv = exp2_approx(__builtin_fmaf(s[qs][r], scale_log2, lv[qs][r]));
-    if constexpr (MASK) {
-      const int qi = qb + 32 * qs + elem_of_reg(r, g);
-      pv = qi < N && (!CAUSAL || krow <= qi) ? pv : 0.f;
-    }
-    pb[2 * qs + (r >> 3)][r & 7] = (__bf16)pv;
-    dsb[2 * qs + (r >> 3)][r & 7] = (__bf16)(pv * (dp[qs][r] - dl[qs][r]));
-  };
-
-  s[0] = s[1] = dp[0] = dp[1] = f32x16{};
-  for_slots<kAhead>([&](auto mc) __attribute__((always_inline)) { reads_of(mc); });
-  __builtin_amdgcn_sched_barrier(0);
-  for_slots<NSLOT>([&](auto mc) __attribute__((always_inline)) {
-    constexpr int m = decltype(mc)::value;
-    product(mc);
-    if constexpr (m + kAhead < NSLOT) reads_of(Slot<m + kAhead>{});
-    if constexpr (m == NM - kSoftRead) read_soft(Slot<0>{});
-    if constexpr (m == 2 * NM - kSoftRead) read_soft(Slot<1>{});
-    if constexpr (m >= NM && m < 2 * NM) {
-      // subtile 0's softmax over subtile 1's products
-      constexpr int E = 16 / NM;
-      for_slots<E>([&](auto ec) __attribute__((always_inline)) {
-        soft(Slot<0>{}, Slot<E * (m - NM) + decltype(ec)::value>{});
-      });
-    } else if constexpr (m >= 2 * NM && m < 2 * NM + 2 * NU) {
-      // subtile 1's softmax over the dV, dK products of queries 0..31
-      constexpr int E = 16 / (2 * NU);
-      for_slots<E>([&](auto ec) __attribute__((always_inline)) {
-        soft(Slot<1>{}, Slot<E * (m - 2 * NM) + decltype(ec)::value>{});
-      });
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  });
-}
+// dkv kernel: a workgroup owns 128 keys; eight waves, two per SIMD, in
+// pairs that share 32 keys (a lane per key).  The first wave of a pair forms
+// S = Q K^T, P = exp2(S scale log2(e) - lse log2(e)) and dV^T += dO^T P; the
+// second forms dP = dO V^T, dS = P o (dP - delta) with P taken from LDS
+// (fp32, lane for lane), and dK^T += Q^T dS.  Each holds one output
+// accumulator and one row operand, which is what lets two waves share a
+// SIMD.  The second wave runs one query block behind the first, so at
+// every step the pair works on different blocks with no wait between them:
+// one wave's matrix products cover the other's softmax arithmetic.  Query
+// blocks therefore live in three LDS buffers (loading, first wave's,
+// second wave's) and P in two.  Query rows of S and dP are permuted so that
+// P and dS land in the B-operand order of the dV and dK products; dO^T and
+// Q^T come through the transposing LDS read.
+constexpr int kDkvWaves = 8;
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) void bwd_dkv_kernel(BwdParams p) {
+__global__ __launch_bounds__(64 * kDkvWaves) void bwd_dkv_kernel(BwdParams p) {
   constexpr int kStep = kStepDkv;
+  static_assert(kStep == 32, "one 32-query subtile per step");
   using G = Geo<D, kStep>;
-  // two buffers, each: Q and dO blocks for the row reads, again for the
-  // transposing reads, then the block's lse and delta
+  constexpr int QST = G::QST, DT = G::DT;
+  // three buffers, each: Q and dO blocks for the row reads, again for the
+  // transposing reads, then 64 lse and 64 delta values (one 4-byte load per
+  // lane; the block uses the first 32); then two P exchange buffers, 16
+  // floats per lane of each pair, stored as four float4 planes
   constexpr int kOffL = 2 * G::kBytesA + 2 * G::kBytesB;
-  constexpr int kBuf = kOffL + 2 * kStep * 4;
-  __shared__ __attribute__((aligned(16))) char smem[2 * kBuf];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int kBuf = kOffL + 2 * 256;
+  constexpr int kOffP = 3 * kBuf;
+  constexpr int kXBuf = 4 * 4096;
+  __shared__ __attribute__((aligned(16))) char smem[kOffP + 2 * kXBuf];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int role = wave >> 2, kg = wave & 3;   // role 0: S, P, dV; role 1: dP, dS, dK
   const int g = lane >> 5, n = lane & 31;
   const int N = p.n;
   int64_t bh;
   int tile;
   tile_of<CAUSAL, true>(p, bh, tile);
   const int k0 = tile * kTile;
-  const int krow = k0 + wave * 32 + n;
+  const int krow = k0 + kg * 32 + n;
   const bool kok = krow < N;
   const int64_t hoff = bh * (int64_t)N * D;
-  i32x4 kv[G::QST], vv[G::QST];
-  load_row<D>(kv, p.k + hoff + (int64_t)krow * D, kok, g);
-  load_row<D>(vv, p.v + hoff + (int64_t)krow * D, kok, g);
-  // The loop's loads are not visible to the compiler's wait counting: its
-  // wait for these rows must fall here, not inside the loop, where it would
-  // also wait for the next block's loads.
-  settle(kv);
-  settle(vv);
-  f32x16 dk[G::DT], dv[G::DT];
+  // K rows (role 0) or V rows (role 1) of this lane's key: the B operand
+  RowRegs<D> kr;
+  load_row<D>(kr, (role == 0 ? p.k : p.v) + hoff + (int64_t)krow * D, kok, g);
+  settle(kr);
+  TileAcc<D> acc;   // dV^T (role 0) or dK^T (role 1)
 #pragma unroll
-  for (int dt = 0; dt < G::DT; ++dt) {
-    dk[dt] = f32x16{};
-    dv[dt] = f32x16{};
-  }
+  for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
   const int a_off = row_lane<D>(n) + 16 * g;
   const int t_off = tr_lane<D>(lane);
+  char* xp = smem + kOffP + kg * 4096 + lane * 16;   // this lane's P exchange slot
   // causal: queries below this tile's first key see none of its keys
   const int qstart = CAUSAL ? k0 : 0;
-  BlockDma<D, kStep> dma;
-  const int wv = __builtin_amdgcn_readfirstlane(wave);
-  dma.init(wv, lane);
-  const i32x4 rsQ = buffer_rsrc(p.q + hoff, (uint32_t)N * G::kRow);
-  const i32x4 rsG = buffer_rsrc(p.d_o + hoff, (uint32_t)N * G::kRow);
-  const i32x4 rsL = buffer_rsrc(p.lse + bh * N, (uint32_t)N * 4);
-  const i32x4 rsD = buffer_rsrc(p.delta + bh * N, (uint32_t)N * 4);
-  static_assert(kStep == 64, "one 4-byte load per lane fills a block's lse or delta");
+  BlockDma<D, kStep, kDkvWaves> dma;
+  dma.init(wave, lane);
+  // the descriptors are uniform: made scalar once here, not at every load
+  const i32x4 rsQ = uniform(buffer_rsrc(p.q + hoff, (uint32_t)N * G::kRow));
+  const i32x4 rsG = uniform(buffer_rsrc(p.d_o + hoff, (uint32_t)N * G::kRow));
+  const i32x4 rsL = uniform(buffer_rsrc(p.lse + bh * N, (uint32_t)N * 4));
+  const i32x4 rsD = uniform(buffer_rsrc(p.delta + bh * N, (uint32_t)N * 4));
   auto issue = [&](int qb, int buf) __attribute__((always_inline)) {
     const uint32_t b = lds_address(smem) + buf * kBuf;
     dma.template issue<true>(rsQ, qb, b, b + 2 * G::kBytesA);
     dma.template issue<true>(rsG, qb, b + G::kBytesA, b + 2 * G::kBytesA + G::kBytesB);
-    if (wv == 0) lds_load4(rsL, (uint32_t)lane * 4, (uint32_t)qb * 4, b + kOffL);
-    if (wv == 1) lds_load4(rsD, (uint32_t)lane * 4, (uint32_t)qb * 4, b + kOffL + kStep * 4);
+    if (wave == 0) lds_load4(rsL, (uint32_t)lane * 4, (uint32_t)qb * 4, b + kOffL);
+    if (wave == 1) lds_load4(rsD, (uint32_t)lane * 4, (uint32_t)qb * 4, b + kOffL + 256);
   };
-  // block qb (in buffer buf) complete and visible; then the next block's
-  // loads into the other buffer, whose last reader was the previous step
-  auto stage = [&](int qb, int buf) __attribute__((always_inline)) {
+  // per-lane values of queries elem_of_reg(r, g) of a block: lse or delta
+  auto row_vals = [&](const char* b, int which, float (&v)[16]) __attribute__((always_inline)) {
+    const float4* v4 = (const float4*)(b + kOffL + which * 256) + 2 * g;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const float4 x = v4[(h & 1) + 4 * (h >> 1)];
+      v[4 * h] = x.x;
+      v[4 * h + 1] = x.y;
+      v[4 * h + 2] = x.z;
+      v[4 * h + 3] = x.w;
+    }
+  };
+  // dV^T += dO^T P (role 0) or dK^T += Q^T dS (role 1): the A operands
+  // (dO^T or Q^T of the block, through the transposing read) in tr
+  using TrRegs = i16x4[2][DT][2];
+  auto read_t = [&](const char* b, TrRegs& tr, auto ic) __attribute__((always_inline)) {
+    constexpr int i = decltype(ic)::value, u = i / DT, dt = i % DT;
+    const char* src = b + 2 * G::kBytesA + (role == 0 ? G::kBytesB : 0) + t_off +
+                      16 * u * G::kStrB + 64 * dt;
+    tr[u][dt][0] = lds_read_tr16(src);
+    tr[u][dt][1] = lds_read_tr16(src + 4 * G::kStrB);
+  };
+  auto outer = [&](const TrRegs& tr, const bf16x8 (&bop)[2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        acc[dt] = mfma_bf16(join_bf16x8(tr[u][dt][0], tr[u][dt][1]), bop[u], acc[dt]);
+  };
+  // S (role 0) or dP (role 1) of the block in b, this lane's key against
+  // queries elem_of_reg(r, g); all A-operand reads go out first, and the
+  // transposing reads of the outer product ride between the products
+  auto inner = [&](const char* b, TrRegs& tr) __attribute__((always_inline)) {
+    const char* ar = b + role * G::kBytesA + a_off;
+    i32x4 a[QST];
+#pragma unroll
+    for (int t = 0; t < QST; ++t) a[t] = *(const i32x4*)(ar + 32 * t);
+    __builtin_amdgcn_sched_barrier(0);
+    f32x16 sd = f32x16{};
+    for_slots<QST>([&](auto tc) __attribute__((always_inline)) {
+      constexpr int t = decltype(tc)::value;
+      sd = mfma_bf16(__builtin_bit_cast(bf16x8, a[t]), __builtin_bit_cast(bf16x8, kr[t]), sd);
+      // 2 DT transposing read pairs over QST = 2 DT products
+      read_t(b, tr, tc);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    return sd;
+  };
+  // Step j: the first wave takes block j, the second block j - 1; block
+  // j + 1 loads meanwhile.  The barrier at the start of a step publishes
+  // block j's loads and P of block j - 1, and retires every read of the
+  // buffers that step j's loads and P writes reuse.  WHO: 0 both waves of
+  // each pair work, 1 only the first (j = 0), 2 only the second (the last
+  // step).  The matrix products sit outside any branch on the role, so the
+  // accumulators keep one register assignment.
+  const int nblk = (N - qstart + kStep - 1) / kStep;
+  int j = 0, buf = 0, prev = 2;   // buf = j % 3, prev = (j - 1) % 3
+  auto step = [&](auto maskc, auto whoc) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(maskc)::value;
+    constexpr int WHO = decltype(whoc)::value;
     wait_loads();
     __syncthreads();
-    if (qb + kStep < N) issue(qb + kStep, buf ^ 1);
+    const int nxt = buf == 2 ? 0 : buf + 1;
+    if (j + 1 < nblk) issue(qstart + (j + 1) * kStep, nxt);
+    if (WHO == 0 || (WHO == 1) == (role == 0)) {
+      const int qb = qstart + (role == 0 ? j : j - 1) * kStep;
+      const char* b = smem + (role == 0 ? buf : prev) * kBuf;
+      TrRegs tr;
+      const f32x16 sd = inner(b, tr);
+      float rv[16];   // lse (role 0) or delta (role 1)
+      row_vals(b, role, rv);
+      bf16x8 bop[2];
+      if (role == 0) {
+        char* xw = xp + (j & 1) * kXBuf;
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          float pv[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * h + e;
+            float t = exp2_approx(__builtin_fmaf(sd[r], p.scale_log2, -kLog2e * rv[r]));
+            if constexpr (MASK) {
+              const int qi = qb + elem_of_reg(r, g);
+              t = qi < N && (!CAUSAL || krow <= qi) ? t : 0.f;
+            }
+            pv[e] = t;
+            bop[r >> 3][r & 7] = (__bf16)t;
+          }
+          *(float4*)(xw + h * 1024) = make_float4(pv[0], pv[1], pv[2], pv[3]);
+        }
+      } else {
+        const char* xr = xp + ((j - 1) & 1) * kXBuf;
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          const float4 pv = *(const float4*)(xr + h * 1024);
+          const float ps[4] = {pv.x, pv.y, pv.z, pv.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * h + e;
+            bop[r >> 3][r & 7] = (__bf16)(ps[e] * (sd[r] - rv[r]));
+          }
+        }
+      }
+      outer(tr, bop);
+    }
+    prev = buf;
+    buf = nxt;
+    ++j;
   };
-  auto run = [&](int qb, int buf, auto maskc) __attribute__((always_inline)) {
-    const char* b = smem + buf * kBuf;
-    dkv_step<D, kStep, CAUSAL, decltype(maskc)::value>(
-        b, (const float*)(b + kOffL), (const float*)(b + kOffL + kStep * 4), a_off, t_off, g, qb,
-        krow, N, p.scale_log2, kv, vv, dk, dv);
-  };
-  // Blocks that need the mask (causal: the two holding this tile's own
+  // Blocks that need the mask (causal: the four holding this tile's own
   // queries; the ragged last block) and the rest run in separate loops, so
-  // that the common one carries no compares and the accumulators keep one
-  // register assignment per loop.
-  const int qfull = CAUSAL ? k0 + kTile : 0;
-  const int nfull = N / kStep * kStep;
+  // that the common one carries no compares.
+  const int jmask = CAUSAL ? min(nblk, kTile / kStep) : 0;
+  const int jfull = min(nblk, max(jmask, (N - qstart) / kStep));
   issue(qstart, 0);
-  int qb = qstart, buf = 0;
-  for (; qb < min(qfull, N); qb += kStep, buf ^= 1) {
-    stage(qb, buf);
-    run(qb, buf, Flag<true>{});
-  }
-  for (; qb < nfull; qb += kStep, buf ^= 1) {
-    stage(qb, buf);
-    run(qb, buf, Flag<false>{});
-  }
-  for (; qb < N; qb += kStep, buf ^= 1) {
-    stage(qb, buf);
-    run(qb, buf, Flag<true>{});
-  }
+  step(Flag<true>{}, Slot<1>{});
+  while (j < jmask) step(Flag<true>{}, Slot<0>{});
+  while (j < jfull) step(Flag<false>{}, Slot<0>{});
+  while (j < nblk) step(Flag<true>{}, Slot<0>{});
+  step(Flag<false>{}, Slot<2>{});
   if (kok) {
-    store_row<D>(p.dk + hoff + (int64_t)krow * D, dk, p.scale, g);
-    store_row<D>(p.dv + hoff + (int64_t)krow * D, dv, 1.0f, g);
+    if (role == 0)
+      store_row<D>(p.dv + hoff + (int64_t)krow * D, acc, 1.0f, g);
+    else
+      store_row<D>(p.dk + hoff + (int64_t)krow * D, acc, p.scale, g);
   }
 }
 
 template <int D, bool CAUSAL>
 hipError_t launch_bwd_dc(const BwdParams& bp, int64_t bh, hipStream_t st) {
   const dim3 grid((unsigned)(bh * bp.tiles));
-  hipLaunchKernelGGL((bwd_dkv_kernel<D, CAUSAL>), grid, dim3(kThreads), 0, st, bp);
+  hipLaunchKernelGGL((bwd_dkv_kernel<D, CAUSAL>), grid, dim3(64 * kDkvWaves), 0, st, bp);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), grid, dim3(kThreads), 0, st, bp);
