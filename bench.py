@@ -39,7 +39,7 @@ HBM_PEAK_GBS = 8000.0
 
 # HBM bytes per launch of the flash kernel on c3, from two rocprofv3 --pmc
 # passes (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch).  A plain 256 MiB
-# device copy reads FETCH_SIZE = 131084 KiB and WRITE_SIZE = 262144 KiB, so
+# device copy reads FETCH_SIZE = 131085 KiB and WRITE_SIZE = 262144 KiB, so
 # FETCH_SIZE is scaled by 2 and WRITE_SIZE by 1.  The figure is valid only for
 # the kernel sources it was taken on (sha256 of the files below).
 TRAFFIC_SOURCES = ("precision_numerics_amd/csrc/flash_fwd.hip",
@@ -48,9 +48,9 @@ TRAFFIC_SOURCES = ("precision_numerics_amd/csrc/flash_fwd.hip",
                    "precision_numerics_amd/csrc/lds_dma.hpp")
 TRAFFIC = {
     "workload": "c3",
-    "sources_sha256": "2caef7d47e60d33024b6cb0ebb18e8f2c3ba7c5c5a7c9627f8cb47fbe73ea4e1",
-    "fetch_kib": 294549.8, "fetch_scale": 2.0,
-    "write_kib": 138753.7, "write_scale": 1.0,
+    "sources_sha256": "2af279e559c79fe423a1f6590c67874f50e5e285474e9708ab0e1d8a64ce1f8c",
+    "fetch_kib": 301626.7, "fetch_scale": 2.0,
+    "write_kib": 138754.2, "write_scale": 1.0,
 }
 
 

@@ -25,8 +25,9 @@
 //               through the transposing LDS read.
 //   dkv kernel: a workgroup owns 128 key rows (a lane per key) and walks the
 //               query blocks: S = Q K^T and dP = dO V^T with permuted query
-//               rows, then dV^T += dO^T P and dK^T += Q^T dS.
-// The blocks of the other operand stream through two LDS buffers by
+//               rows, then dV^T += dO^T P and dK^T += Q^T dS, split between
+//               the two waves of a pair (S, P, dV / dP, dS, dK).
+// The blocks of the other operand stream through LDS buffers by
 // buffer-to-LDS loads: the loads of block j + 1 run while block j's
 // products do (zeros past N); the per-row lse and delta of a query block
 // sit in LDS beside it.
@@ -37,7 +38,7 @@
 namespace pn {
 namespace {
 
-constexpr int kThreads = 256;   // four waves
+constexpr int kThreads = 256;   // four waves (dq kernel)
 constexpr int kTile = 128;      // rows a workgroup owns (32 per wave)
 // Rows of the other operand per step (both kernels run two waves per SIMD,
 // one covering the other's latencies).
