@@ -109,6 +109,31 @@ def test_backward_d128_many_blocks(lib, causal):
                    f"rel mean {rel[1]:.2e}")
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_head_groups(lib, causal):
+    """Nine (batch, head) units: the kernels take heads in groups of eight
+    (one per XCD) and the ninth on its own, so both branches of the
+    workgroup-to-tile map run in one launch; every head is checked."""
+    import precision_numerics_amd as pna
+    n, d, units = 300, 64, 9
+    cfg = synth.small(synth.CONFIGS["c2"], batch=3, heads=3, seq_len=n, head_dim=d,
+                      causal=causal)
+    inp = synth.make_inputs(cfg, seed=55)
+    q, k, v = device_inputs(inp)
+    o, d_o, grads = _grads(pna, q, k, v, causal, seed=5)
+    qf, kf, vf = (x.reshape(units, n, d) for x in oracle_inputs(inp))
+    of = out_to_f64(o).reshape(units, n, d)
+    gf = out_to_f64(d_o).reshape(units, n, d)
+    sc = oracle.default_scale(d)
+    for u in range(units):
+        ref = oracle.attention_backward_head(qf[u], kf[u], vf[u], of[u], gf[u], causal=causal,
+                                             scale=sc)
+        atols = (_atol(d, sc, kf[u], gf[u], vf[u]), _atol(d, sc, qf[u], gf[u], vf[u]), 0.0)
+        for i, name in enumerate(("dq", "dk", "dv")):
+            _check(out_to_f64(grads[i]).reshape(units, n, d)[u], ref[i], f"{name} u={u}", atols[i])
+    _print(f"backward 9 heads causal={causal}: all units within tolerance")
+
+
 def test_backward_workload_shape(lib):
     """The GPT-2-small workload's shape (B8 H12 N1024 d64, causal), sampled
     heads against the oracle, and bitwise reproducible run to run."""
