@@ -96,22 +96,36 @@ __device__ __forceinline__ void tile_of(const BwdParams& p, int64_t& bh, int& ti
 }
 
 template <int D, int STEP> struct Geo {
-  static constexpr int kRow = D * 2;         // bf16 row bytes
-  // Each block sits in LDS twice, with two row paddings: 16 bytes for the
-  // row reads of the A operands (16 lanes read one 16-byte column of 16
-  // rows: the rows then fall on distinct banks) and 64 bytes for the
-  // transposing reads (lanes read 8-byte pieces of four rows, 64 bytes
-  // apart within each row).
-  static constexpr int kStrA = kRow + 16;
-  static constexpr int kStrB = kRow + 64;
-  // 1 KB load segments per copy, and the copy's LDS bytes (whole segments)
-  static constexpr int kSegA = (STEP * kStrA + 1023) / 1024;
-  static constexpr int kSegB = (STEP * kStrB + 1023) / 1024;
-  static constexpr int kBytesA = kSegA * 1024;
-  static constexpr int kBytesB = kSegB * 1024;
-  static constexpr int QST = D / 16;         // 16-element chunks of a row
-  static constexpr int DT = D / 32;          // 32-row subtiles of a transposed output
+  static constexpr int kRow = D * 2;           // bf16 row bytes
+  static constexpr int kBytes = STEP * kRow;   // one block in LDS, unpadded
+  static constexpr int kSeg = kBytes / 1024;   // 1 KB load segments
+  static_assert(kBytes % 1024 == 0, "a block is whole load segments");
+  static constexpr int QST = D / 16;           // 16-element chunks of a row
+  static constexpr int DT = D / 32;            // 32-row subtiles of a transposed output
 };
+
+// LDS layout of a block: row R at R * 2D bytes, its 16-byte chunk c at chunk
+// position c ^ swz(R).  Both read patterns then miss bank conflicts:
+// 16 lanes reading one chunk of 16 different rows (the A-operand row reads)
+// land on 16 distinct chunk positions (swz is one-to-one on the low four
+// row bits for d = 128, and on rows of one parity for d = 64, where two
+// rows share a 256-byte bank sweep), and 32 lanes reading 8-byte pieces of
+// chunks 4dt .. 4dt + 3 of four consecutive rows (the transposing read)
+// land on 32 distinct 8-byte slots (swz moves consecutive rows to different
+// groups of four chunks).
+template <int D> __device__ __forceinline__ int swz(int R) {
+  if constexpr (D == 128) return ((R & 3) << 2) | ((R >> 2) & 3);
+  else return (((R >> 1) & 1) << 2) | ((R >> 2) & 3);
+}
+
+// Source offset, inside a block's rows, of the 16 bytes that lane `lane` of
+// load segment `seg` writes at LDS position (seg * 64 + lane) * 16.
+template <int D> __device__ __forceinline__ uint32_t swz_src_offset(int seg, int lane) {
+  constexpr int kRow = 2 * D;
+  const int pos = (seg * 64 + lane) * 16;
+  const int R = pos / kRow, cpos = (pos % kRow) / 16;
+  return (uint32_t)(R * kRow + 16 * (cpos ^ swz<D>(R)));
+}
 
 template <int I> struct Slot { static constexpr int value = I; };
 template <bool B> struct Flag { static constexpr bool value = B; };
@@ -125,42 +139,30 @@ __device__ __forceinline__ void for_slots(F&& f) {
   }
 }
 
-// This wave's share of the buffer-to-LDS loads that fill the two LDS copies
-// of a STEP-row block of a [N][D] bf16 matrix, among W issuing waves:
-// segments w, w + W, .. of each copy, with each lane's source offset inside
-// the block (rows past N read zeros through the buffer range check).
-// Asynchronous: the loads are awaited by an explicit s_waitcnt vmcnt(0)
-// before the barrier that publishes the block.
+// This wave's share of the buffer-to-LDS loads that fill the LDS image of a
+// STEP-row block of a [N][D] bf16 matrix, among W issuing waves: segments
+// w, w + W, .., with each lane's source offset inside the block (rows past N
+// read zeros through the buffer range check).  Asynchronous: the loads are
+// awaited by an explicit s_waitcnt vmcnt(0) before the barrier that
+// publishes the block.
 template <int D, int STEP, int W> struct BlockDma {
   using G = Geo<D, STEP>;
-  static constexpr int kPerA = (G::kSegA + W - 1) / W;
-  static constexpr int kPerB = (G::kSegB + W - 1) / W;
-  uint32_t offA[kPerA], offB[kPerB];
+  static constexpr int kPer = (G::kSeg + W - 1) / W;
+  uint32_t off[kPer];
   int wave;
   __device__ __forceinline__ void init(int w, int lane) {
     wave = w;
 #pragma unroll
-    for (int i = 0; i < kPerA; ++i) offA[i] = seg_src_offset(w + W * i, lane, G::kRow, G::kStrA);
-#pragma unroll
-    for (int i = 0; i < kPerB; ++i) offB[i] = seg_src_offset(w + W * i, lane, G::kRow, G::kStrB);
+    for (int i = 0; i < kPer; ++i) off[i] = swz_src_offset<D>(w + W * i, lane);
   }
-  // rows r0.. into the row-read copy at LDS address lds_a and, if B_COPY,
-  // the transposing-read copy at lds_b
-  template <bool B_COPY>
-  __device__ __forceinline__ void issue(i32x4 rs, int r0, uint32_t lds_a, uint32_t lds_b) const {
+  // rows r0.. into the block image at LDS address lds
+  __device__ __forceinline__ void issue(i32x4 rs, int r0, uint32_t lds) const {
     const uint32_t soff = (uint32_t)r0 * G::kRow;
-    for_slots<kPerA>([&](auto ic) __attribute__((always_inline)) {
+    for_slots<kPer>([&](auto ic) __attribute__((always_inline)) {
       constexpr int i = decltype(ic)::value;
-      if (W * i + W - 1 < G::kSegA || wave + W * i < G::kSegA)
-        lds_load16<i * W * 1024>(rs, offA[i], soff, lds_a + wave * 1024);
+      if (W * i + W - 1 < G::kSeg || wave + W * i < G::kSeg)
+        lds_load16<i * W * 1024>(rs, off[i], soff, lds + wave * 1024);
     });
-    if constexpr (B_COPY) {
-      for_slots<kPerB>([&](auto ic) __attribute__((always_inline)) {
-        constexpr int i = decltype(ic)::value;
-        if (W * i + W - 1 < G::kSegB || wave + W * i < G::kSegB)
-          lds_load16<i * W * 1024>(rs, offB[i], soff, lds_b + wave * 1024);
-      });
-    }
   }
 };
 
@@ -205,23 +207,35 @@ __device__ __forceinline__ void store_row(uint16_t* dst, const TileAcc<D>& acc, 
     }
 }
 
-// lanes' LDS byte offsets: permuted A-operand rows, and the transposing read
-template <int D>
-__device__ __forceinline__ int row_lane(int n) { return perm_row(n) * Geo<D, 64>::kStrA; }
-template <int D>
-__device__ __forceinline__ int tr_lane(int lane) {
-  const int g = lane >> 5;
-  return (8 * g + ((lane & 15) >> 2)) * Geo<D, 64>::kStrB +
-         (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
-}
+// This lane's LDS byte offsets inside a block image: the A-operand row
+// reads (row perm_row(n), chunk 2t + g, t = 0 .. D/16 - 1) and the
+// transposing reads (8 bytes of rows 8g + (lane%16)/4 + 4hi, at byte column
+// 64dt + 32((lane/16)%2) + 8(lane%4)); 16 more rows add 16 * 2D bytes.
+template <int D> struct LaneAddr {
+  int row[D / 16];
+  int tr[D / 32][2];
+  __device__ __forceinline__ void init(int lane) {
+    const int g = lane >> 5, n = lane & 31;
+    const int R = perm_row(n);
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) row[t] = R * 2 * D + 16 * ((2 * t + g) ^ swz<D>(R));
+    const int k = (lane & 15) >> 2, h = (lane >> 4) & 1, c = lane & 3;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int hi = 0; hi < 2; ++hi) {
+        const int r = 8 * g + k + 4 * hi;
+        tr[dt][hi] = r * 2 * D + 16 * ((4 * dt + 2 * h + (c >> 1)) ^ swz<D>(r)) + 8 * (c & 1);
+      }
+  }
+};
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p) {
   constexpr int kStep = kStepDq;
   using G = Geo<D, kStep>;
-  // two buffers, each: K and V blocks for the row reads, K again for the
-  // transposing reads
-  constexpr int kBuf = 2 * G::kBytesA + G::kBytesB;
+  // two buffers, each: the K and V blocks
+  constexpr int kBuf = 2 * G::kBytes;
   __shared__ __attribute__((aligned(16))) char smem[2 * kBuf];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 5, n = lane & 31;
@@ -248,8 +262,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
   for (int dt = 0; dt < G::DT; ++dt) dq[dt] = f32x16{};
   const int kend = CAUSAL ? min(N, q0 + kTile) : N;
-  const int a_off = row_lane<D>(n) + 16 * g;
-  const int t_off = tr_lane<D>(lane);
+  LaneAddr<D> la;
+  la.init(lane);
   BlockDma<D, kStep, 4> dma;
   dma.init(__builtin_amdgcn_readfirstlane(wave), lane);
   // the descriptors are uniform: made scalar once here, not at every load
@@ -257,8 +271,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p) {
   const i32x4 rsV = uniform(buffer_rsrc(p.v + hoff, (uint32_t)N * G::kRow));
   auto issue = [&](int kb, int buf) __attribute__((always_inline)) {
     const uint32_t b = lds_address(smem) + buf * kBuf;
-    dma.template issue<true>(rsK, kb, b, b + 2 * G::kBytesA);
-    dma.template issue<false>(rsV, kb, b + G::kBytesA, 0);
+    dma.issue(rsK, kb, b);
+    dma.issue(rsV, kb, b + G::kBytes);
   };
   // block kb (in buffer buf) complete and visible; then the next block's
   // loads into the other buffer, whose last reader was the previous step
@@ -275,13 +289,13 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p) {
     for (int ks = 0; ks < kStep / 32; ++ks) {
       s[ks] = f32x16{};
       dp[ks] = f32x16{};
-      const char* kr = smem_b + ks * 32 * G::kStrA + a_off;
-      const char* vr = smem_b + G::kBytesA + ks * 32 * G::kStrA + a_off;
+      const char* kr = smem_b + ks * 32 * G::kRow;
+      const char* vr = smem_b + G::kBytes + ks * 32 * G::kRow;
 #pragma unroll
       for (int t = 0; t < G::QST; ++t) {
-        s[ks] = mfma_bf16(__builtin_bit_cast(bf16x8, *(const i32x4*)(kr + 32 * t)),
+        s[ks] = mfma_bf16(__builtin_bit_cast(bf16x8, *(const i32x4*)(kr + la.row[t])),
                           __builtin_bit_cast(bf16x8, qv[t]), s[ks]);
-        dp[ks] = mfma_bf16(__builtin_bit_cast(bf16x8, *(const i32x4*)(vr + 32 * t)),
+        dp[ks] = mfma_bf16(__builtin_bit_cast(bf16x8, *(const i32x4*)(vr + la.row[t])),
                            __builtin_bit_cast(bf16x8, gv[t]), dp[ks]);
       }
     }
@@ -302,9 +316,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p) {
     for (int u = 0; u < kStep / 16; ++u)
 #pragma unroll
       for (int dt = 0; dt < G::DT; ++dt) {
-        const char* src = smem_b + 2 * G::kBytesA + t_off + 16 * u * G::kStrB + 64 * dt;
-        const i16x4 lo = lds_read_tr16(src);
-        const i16x4 hi = lds_read_tr16(src + 4 * G::kStrB);
+        const char* src = smem_b + 16 * u * G::kRow;
+        const i16x4 lo = lds_read_tr16(src + la.tr[dt][0]);
+        const i16x4 hi = lds_read_tr16(src + la.tr[dt][1]);
         dq[dt] = mfma_bf16(join_bf16x8(lo, hi), dsb[u], dq[dt]);
       }
   };
@@ -346,11 +360,11 @@ __global__ __launch_bounds__(64 * kDkvWaves) void bwd_dkv_kernel(BwdParams p) {
   static_assert(kStep == 32, "one 32-query subtile per step");
   using G = Geo<D, kStep>;
   constexpr int QST = G::QST, DT = G::DT;
-  // three buffers, each: Q and dO blocks for the row reads, again for the
-  // transposing reads, then 64 lse and 64 delta values (one 4-byte load per
-  // lane; the block uses the first 32); then two P exchange buffers, 16
-  // floats per lane of each pair, stored as four float4 planes
-  constexpr int kOffL = 2 * G::kBytesA + 2 * G::kBytesB;
+  // three buffers, each: the Q and dO blocks, then 64 lse and 64 delta
+  // values (one 4-byte load per lane; the block uses the first 32); then
+  // two P exchange buffers, 16 floats per lane of each pair, stored as four
+  // float4 planes
+  constexpr int kOffL = 2 * G::kBytes;
   constexpr int kBuf = kOffL + 2 * 256;
   constexpr int kOffP = 3 * kBuf;
   constexpr int kXBuf = 4 * 4096;
@@ -374,8 +388,8 @@ __global__ __launch_bounds__(64 * kDkvWaves) void bwd_dkv_kernel(BwdParams p) {
   TileAcc<D> acc;   // dV^T (role 0) or dK^T (role 1)
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
-  const int a_off = row_lane<D>(n) + 16 * g;
-  const int t_off = tr_lane<D>(lane);
+  LaneAddr<D> la;
+  la.init(lane);
   char* xp = smem + kOffP + kg * 4096 + lane * 16;   // this lane's P exchange slot
   // causal: queries below this tile's first key see none of its keys
   const int qstart = CAUSAL ? k0 : 0;
@@ -388,8 +402,8 @@ __global__ __launch_bounds__(64 * kDkvWaves) void bwd_dkv_kernel(BwdParams p) {
   const i32x4 rsD = uniform(buffer_rsrc(p.delta + bh * N, (uint32_t)N * 4));
   auto issue = [&](int qb, int buf) __attribute__((always_inline)) {
     const uint32_t b = lds_address(smem) + buf * kBuf;
-    dma.template issue<true>(rsQ, qb, b, b + 2 * G::kBytesA);
-    dma.template issue<true>(rsG, qb, b + G::kBytesA, b + 2 * G::kBytesA + G::kBytesB);
+    dma.issue(rsQ, qb, b);
+    dma.issue(rsG, qb, b + G::kBytes);
     if (wave == 0) lds_load4(rsL, (uint32_t)lane * 4, (uint32_t)qb * 4, b + kOffL);
     if (wave == 1) lds_load4(rsD, (uint32_t)lane * 4, (uint32_t)qb * 4, b + kOffL + 256);
   };
@@ -410,10 +424,9 @@ __global__ __launch_bounds__(64 * kDkvWaves) void bwd_dkv_kernel(BwdParams p) {
   using TrRegs = i16x4[2][DT][2];
   auto read_t = [&](const char* b, TrRegs& tr, auto ic) __attribute__((always_inline)) {
     constexpr int i = decltype(ic)::value, u = i / DT, dt = i % DT;
-    const char* src = b + 2 * G::kBytesA + (role == 0 ? G::kBytesB : 0) + t_off +
-                      16 * u * G::kStrB + 64 * dt;
-    tr[u][dt][0] = lds_read_tr16(src);
-    tr[u][dt][1] = lds_read_tr16(src + 4 * G::kStrB);
+    const char* src = b + (role == 0 ? G::kBytes : 0) + 16 * u * G::kRow;
+    tr[u][dt][0] = lds_read_tr16(src + la.tr[dt][0]);
+    tr[u][dt][1] = lds_read_tr16(src + la.tr[dt][1]);
   };
   auto outer = [&](const TrRegs& tr, const bf16x8 (&bop)[2]) __attribute__((always_inline)) {
 #pragma unroll
@@ -426,10 +439,10 @@ __global__ __launch_bounds__(64 * kDkvWaves) void bwd_dkv_kernel(BwdParams p) {
   // queries elem_of_reg(r, g); all A-operand reads go out first, and the
   // transposing reads of the outer product ride between the products
   auto inner = [&](const char* b, TrRegs& tr) __attribute__((always_inline)) {
-    const char* ar = b + role * G::kBytesA + a_off;
+    const char* ar = b + role * G::kBytes;
     i32x4 a[QST];
 #pragma unroll
-    for (int t = 0; t < QST; ++t) a[t] = *(const i32x4*)(ar + 32 * t);
+    for (int t = 0; t < QST; ++t) a[t] = *(const i32x4*)(ar + la.row[t]);
     __builtin_amdgcn_sched_barrier(0);
     f32x16 sd = f32x16{};
     for_slots<QST>([&](auto tc) __attribute__((always_inline)) {
