@@ -233,6 +233,8 @@ def main():
                     help="(batch, head) units in the oracle sample (0: skip the CPU leg)")
     ap.add_argument("--cpu-workers", type=int, default=16)
     ap.add_argument("--no-legs", action="store_true", help="time the flash kernel only")
+    ap.add_argument("--legs", default="all",
+                    help="comma-separated legs to run after the flash kernel (default: all)")
     ap.add_argument("--copy-probe", action="store_true")
     args = ap.parse_args()
 
@@ -326,7 +328,7 @@ def main():
         result["gpu_over_cpu"] = round(tflops / cpu["value"], 1)
         ref_t = torch.from_numpy(ref).cuda()
         bias_refs = None
-        if not args.no_legs:
+        if not args.no_legs and (args.legs == "all" or "rounding_bias" in args.legs.split(",")):
             log("bench: FP64 oracle references for the rounding-bias leg")
             bias_refs = cpu_baseline_bias_refs(workers)
     else:
@@ -338,7 +340,12 @@ def main():
     if not args.no_legs:
         legs = {}
         ob_s = None
+
+        def want(name):
+            return args.legs == "all" or name in args.legs.split(",")
         try:
+            if not want("baseline"):
+                raise LookupError
             log("bench: baseline attention leg")
             prob = pna.make_problem(q, causal=cfg.causal, p_bf16=p_bf16)
             ws = torch.empty(pna.attn_baseline_workspace_size(prob), dtype=torch.uint8,
@@ -363,9 +370,11 @@ def main():
                 legs["baseline"]["max_abs_err"] = dvb["max_abs"]
                 legs["baseline"]["mean_abs_err"] = dvb["mean_abs"]
             del ws
+        except LookupError:
+            pass
         except Exception as exc:                         # noqa: BLE001
             legs["baseline"] = {"error": repr(exc)}
-        if ref_t is not None:
+        if ref_t is not None and want("deviation"):
             try:
                 log("bench: deviation leg")
                 scratch = torch.empty(pna.attn_deviation_scratch_size(ref_t.numel()),
@@ -377,7 +386,7 @@ def main():
                                      "note": "includes the host synchronisation per call"}
             except Exception as exc:                     # noqa: BLE001
                 legs["deviation"] = {"error": repr(exc)}
-        if ref_t is not None:
+        if ref_t is not None and want("wasserstein"):
             try:
                 log("bench: Wasserstein leg")
                 ws_b = torch.empty(pna.attn_wasserstein_scratch_size(
@@ -398,13 +407,15 @@ def main():
                 del ws_b
             except Exception as exc:                     # noqa: BLE001
                 legs["wasserstein"] = {"error": repr(exc)}
-        if bias_refs is not None:
+        if bias_refs is not None and want("rounding_bias"):
             try:
                 log("bench: rounding-bias leg (c4, standard vs stabilised)")
                 legs["rounding_bias"] = bias_leg(pna, torch, bias_refs)
             except Exception as exc:                     # noqa: BLE001
                 legs["rounding_bias"] = {"error": repr(exc)}
         try:
+            if not want("bwd_delta"):
+                raise LookupError
             log("bench: delta = rowsum(dO * O) leg")
             g = torch.randn(out.shape, device="cuda").to(out.dtype)
             dl = torch.empty(out.shape[:-1], dtype=torch.float32, device="cuda")
@@ -413,9 +424,11 @@ def main():
             legs["bwd_delta"] = {"ms": round(dms, 4), "alg_bytes": nb,
                                  "GB_per_s": round(nb / (dms * 1e-3) / 1e9, 1),
                                  "hbm_frac": round(nb / (dms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        except LookupError:
+            pass
         except Exception as exc:                         # noqa: BLE001
             legs["bwd_delta"] = {"error": repr(exc)}
-        if cfg.dtype == "bf16":
+        if cfg.dtype == "bf16" and want("flash_backward"):
             try:
                 log("bench: flash backward leg")
                 lse_b = torch.empty(q.shape[:-1], dtype=torch.float32, device="cuda")
@@ -439,6 +452,8 @@ def main():
             except Exception as exc:                     # noqa: BLE001
                 legs["flash_backward"] = {"error": repr(exc)}
         try:
+            if not want("flash_fp8"):
+                raise LookupError
             log("bench: fp8 (E4M3) Q/K flash leg on the int8 workload's shape")
             c5 = synth.CONFIGS["c5"]
             in5 = synth.make_inputs(c5)
@@ -456,9 +471,13 @@ def main():
                                  "tflops": round(f5 / (fms * 1e-3) / 1e12, 2),
                                  "frac_of_fp8_bf16_peak": round(ideal / fms, 4)}
             del q8, k8, v8, o8, in5
+        except LookupError:
+            pass
         except Exception as exc:                         # noqa: BLE001
             legs["flash_fp8"] = {"error": repr(exc)}
         try:
+            if not want("quantize_int8"):
+                raise LookupError
             log("bench: int8 quantiser leg")
             x = torch.randn(cfg.batch * cfg.heads * cfg.seq_len, cfg.head_dim, device="cuda")
             codes = torch.empty(x.shape, dtype=torch.int8, device="cuda")
@@ -468,6 +487,8 @@ def main():
             nb = x.numel() * 5 + x.shape[0] * 4
             legs["quantize_int8"] = {"ms": round(qms, 4), "alg_bytes": nb,
                                      "GB_per_s": round(nb / (qms * 1e-3) / 1e9, 1)}
+        except LookupError:
+            pass
         except Exception as exc:                         # noqa: BLE001
             legs["quantize_int8"] = {"error": repr(exc)}
         result["legs"] = legs
