@@ -56,7 +56,8 @@ struct BwdParams {
   uint16_t* dk;
   uint16_t* dv;
   int n;
-  int tiles;          // 128-row tiles per head
+  int tiles;          // 128-query tiles per head (dq kernel)
+  int tiles_kv;       // key tiles per head (dkv kernel)
   int bh_count;       // batch * heads
   float scale;
   float scale_log2;   // scale * log2(e)
@@ -73,14 +74,13 @@ __device__ __forceinline__ int elem_of_reg(int r, int g) { return 16 * (r >> 3) 
 // heads are taken in groups of eight, head 8c + x on XCD x: each XCD then
 // works through its heads one at a time, all tiles of a head together, and
 // the head's K, V, Q, dO rows stay in that XCD's L2.  Within a head,
-// causal tiles differ in length (the dkv kernel's tile t walks N - 128 t
+// causal tiles differ in length (the dkv kernel's tile t walks N - 64 t
 // queries, the dq kernel's 128 (t + 1) keys) and go out longest first, so
 // short ones fill the machine at the end.  Heads past the last whole group
 // of eight follow one after another.
 template <bool CAUSAL, bool LONG_FIRST_LOW>
-__device__ __forceinline__ void tile_of(const BwdParams& p, int64_t& bh, int& tile) {
+__device__ __forceinline__ void tile_of(const BwdParams& p, int T, int64_t& bh, int& tile) {
   const int64_t b = blockIdx.x;
-  const int T = p.tiles;
   const int64_t grouped = (int64_t)(p.bh_count / 8) * 8 * T;
   int t;
   if (b < grouped) {
@@ -242,7 +242,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p) {
   const int N = p.n;
   int64_t bh;
   int tile;
-  tile_of<CAUSAL, false>(p, bh, tile);
+  tile_of<CAUSAL, false>(p, p.tiles, bh, tile);
   const int q0 = tile * kTile;
   const int qrow = q0 + wave * 32 + n;
   const bool qok = qrow < N;
@@ -339,23 +339,26 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p) {
   if (qok) store_row<D>(p.dq + hoff + (int64_t)qrow * D, dq, p.scale, g);
 }
 
-// dkv kernel: a workgroup owns 128 keys; eight waves, two per SIMD, in
-// pairs that share 32 keys (a lane per key).  The first wave of a pair forms
-// S = Q K^T, P = exp2(S scale log2(e) - lse log2(e)) and dV^T += dO^T P; the
-// second forms dP = dO V^T, dS = P o (dP - delta) with P taken from LDS
-// (fp32, lane for lane), and dK^T += Q^T dS.  Each holds one output
-// accumulator and one row operand, which is what lets two waves share a
-// SIMD.  The second wave runs one query block behind the first, so at
+// dkv kernel: a workgroup owns 64 keys; four waves in two pairs that share
+// 32 keys each (a lane per key), two workgroups per compute unit, so one
+// workgroup's barrier waits are filled by the other's work.  The first wave
+// of a pair forms S = Q K^T, P = exp2(S scale log2(e) - lse log2(e)) and
+// dV^T += dO^T P; the second forms dP = dO V^T, dS = P o (dP - delta) with P
+// taken from LDS (fp32, lane for lane), and dK^T += Q^T dS.  Each holds one
+// output accumulator and one row operand, which is what lets two waves
+// share a SIMD.  The second wave runs one query block behind the first, so at
 // every step the pair works on different blocks with no wait between them:
 // one wave's matrix products cover the other's softmax arithmetic.  Query
 // blocks therefore live in three LDS buffers (loading, first wave's,
 // second wave's) and P in two.  Query rows of S and dP are permuted so that
 // P and dS land in the B-operand order of the dV and dK products; dO^T and
 // Q^T come through the transposing LDS read.
-constexpr int kDkvWaves = 8;
+constexpr int kDkvWaves = 4;                  // two pairs
+constexpr int kDkvPairs = kDkvWaves / 2;
+constexpr int kDkvTile = 32 * kDkvPairs;      // keys a workgroup owns
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(64 * kDkvWaves) void bwd_dkv_kernel(BwdParams p) {
+__global__ __launch_bounds__(64 * kDkvWaves, 2) void bwd_dkv_kernel(BwdParams p) {
   constexpr int kStep = kStepDkv;
   static_assert(kStep == 32, "one 32-query subtile per step");
   using G = Geo<D, kStep>;
@@ -367,17 +370,18 @@ __global__ __launch_bounds__(64 * kDkvWaves) void bwd_dkv_kernel(BwdParams p) {
   constexpr int kOffL = 2 * G::kBytes;
   constexpr int kBuf = kOffL + 2 * 256;
   constexpr int kOffP = 3 * kBuf;
-  constexpr int kXBuf = 4 * 4096;
+  constexpr int kXBuf = kDkvPairs * 4096;
   __shared__ __attribute__((aligned(16))) char smem[kOffP + 2 * kXBuf];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
-  const int role = wave >> 2, kg = wave & 3;   // role 0: S, P, dV; role 1: dP, dS, dK
+  // role 0: S, P, dV; role 1: dP, dS, dK; kg: the pair
+  const int role = wave / kDkvPairs, kg = wave % kDkvPairs;
   const int g = lane >> 5, n = lane & 31;
   const int N = p.n;
   int64_t bh;
   int tile;
-  tile_of<CAUSAL, true>(p, bh, tile);
-  const int k0 = tile * kTile;
+  tile_of<CAUSAL, true>(p, p.tiles_kv, bh, tile);
+  const int k0 = tile * kDkvTile;
   const int krow = k0 + kg * 32 + n;
   const bool kok = krow < N;
   const int64_t hoff = bh * (int64_t)N * D;
@@ -515,10 +519,10 @@ __global__ __launch_bounds__(64 * kDkvWaves) void bwd_dkv_kernel(BwdParams p) {
     buf = nxt;
     ++j;
   };
-  // Blocks that need the mask (causal: the four holding this tile's own
+  // Blocks that need the mask (causal: the two holding this tile's own
   // queries; the ragged last block) and the rest run in separate loops, so
   // that the common one carries no compares.
-  const int jmask = CAUSAL ? min(nblk, kTile / kStep) : 0;
+  const int jmask = CAUSAL ? min(nblk, kDkvTile / kStep) : 0;
   const int jfull = min(nblk, max(jmask, (N - qstart) / kStep));
   issue(qstart, 0);
   step(Flag<true>{}, Slot<1>{});
@@ -536,8 +540,9 @@ __global__ __launch_bounds__(64 * kDkvWaves) void bwd_dkv_kernel(BwdParams p) {
 
 template <int D, bool CAUSAL>
 hipError_t launch_bwd_dc(const BwdParams& bp, int64_t bh, hipStream_t st) {
+  const dim3 grid_kv((unsigned)(bh * bp.tiles_kv));
+  hipLaunchKernelGGL((bwd_dkv_kernel<D, CAUSAL>), grid_kv, dim3(64 * kDkvWaves), 0, st, bp);
   const dim3 grid((unsigned)(bh * bp.tiles));
-  hipLaunchKernelGGL((bwd_dkv_kernel<D, CAUSAL>), grid, dim3(64 * kDkvWaves), 0, st, bp);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), grid, dim3(kThreads), 0, st, bp);
@@ -563,6 +568,7 @@ hipError_t launch_flash_bwd(const AttnBwdArgs& a, hipStream_t st) {
   bp.dv = (uint16_t*)a.dv;
   bp.n = (int)a.seq_len;
   bp.tiles = (int)((a.seq_len + kTile - 1) / kTile);
+  bp.tiles_kv = (int)((a.seq_len + kDkvTile - 1) / kDkvTile);
   bp.bh_count = (int)bh;
   bp.scale = a.scale;
   bp.scale_log2 = (float)((double)a.scale * 1.4426950408889634);
