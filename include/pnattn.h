@@ -87,6 +87,11 @@ typedef struct {
                           r_m < 0 (r_m = 0 keeps 0), so that no unnormalised
                           probability is exactly 1.  Occurrences are counted
                           online over the key blocks processed so far.
+                          Range guard: the normaliser is capped at
+                          r_m + 64 ln 2 (64 in log2 units), so the largest
+                          probability stays >= 2^-64 where the rule alone
+                          would underflow every exp in fp32 (r_m >~ 44/(beta-1)
+                          or r_m <~ -44) and give 0/0.
                           attn_fwd_flash with ATTN_BF16 only (ATTN_ERR_
                           UNSUPPORTED otherwise; attn_fwd_baseline rejects
                           it).  The output equals softmax(S)V in exact
@@ -116,11 +121,13 @@ attn_status_t attn_fwd_flash(const attn_problem_t* prob, const void* q,
                              const float* q_scale, const float* k_scale,
                              void* o, float* lse, void* stream);
 
-/* Debug form of the int8 flash kernel: the same kernel instance also writes
- * each int32 score tile Qc Kc^T it computes (before scaling) to
- * s_out [B,H,N,N] int32 (entries the kernel never computes, e.g. masked
- * causal blocks, are left untouched).  ATTN_INT8 only; for checking that the
- * integer products are exact ("INT-FlashAttention", abstract).           */
+/* Debug form of the int8 flash kernel: a separate instance of the same
+ * kernel template (same tiles, schedule and arithmetic, compiled with one
+ * extra store) that also writes each int32 score tile Qc Kc^T it computes
+ * (before scaling) to s_out [B,H,N,N] int32 (entries the kernel never
+ * computes, e.g. masked causal blocks, are left untouched); its o is
+ * bitwise the production instance's.  ATTN_INT8 only; for checking that
+ * the integer products are exact ("INT-FlashAttention", abstract).       */
 attn_status_t attn_fwd_flash_debug_s(const attn_problem_t* prob, const void* q,
                                      const void* k, const void* v,
                                      const float* q_scale,
@@ -278,6 +285,18 @@ attn_status_t attn_quantize_int8_tiles(const float* x, int64_t groups, int64_t n
  * codes: [rows][d] uint8, scales: [rows] fp32.  1 <= d <= 1024.           */
 attn_status_t attn_quantize_fp8(const float* x, int64_t rows, int64_t d,
                                 uint8_t* codes, float* scales, void* stream);
+
+/* Measurement aid: samples of the shader clock, for reading a timed region
+ * against the clock it ran at (the power controller lowers the shader clock
+ * under sustained matrix work).  Launches `slots` workgroups on stream;
+ * each writes (location, 64-bit shader-clock counter s_memtime, 100 MHz
+ * real-time counter s_memrealtime) to out[3*i .. 3*i+2], where location =
+ * XCD id << 8 | HW_ID bits 8..15 (CU, shader array, shader engine).  The
+ * counters of different CUs are not synchronised, so two calls are
+ * compared on the same location: clock = 100 MHz * d(memtime) /
+ * d(realtime).  A few hundred slots cover every CU.
+ *   out  : device buffer of 3*slots uint64_t;  1 <= slots <= 4096.       */
+attn_status_t attn_clock_sample(uint64_t* out, int32_t slots, void* stream);
 
 const char* attn_status_string(attn_status_t status);
 /* Detail of the last failing call on this thread ("" if none).           */

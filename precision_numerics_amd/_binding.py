@@ -93,6 +93,7 @@ _SIGNATURES = {
                                       ctypes.POINTER(ctypes.c_size_t)],
     "attn_wasserstein": [_P, ctypes.c_int32, _P, ctypes.c_int32, ctypes.c_int64, _P,
                          ctypes.c_size_t, ctypes.POINTER(AttnWasserstein), _P],
+    "attn_clock_sample": [_P, ctypes.c_int32, _P],
     "attn_status_string": [ctypes.c_int],
     "attn_last_error": [],
     "attn_version": [],
@@ -160,6 +161,53 @@ def _contig(*ts):
             raise ValueError("tensors must be contiguous CUDA tensors")
 
 
+def _expect(t, name, shape, dtypes, like=None, required=True):
+    """Raise before any C call when tensor ``t`` does not have the shape and
+    one of the dtypes the kernels will assume for it (the C ABI sees only
+    pointers, so a mismatch here would make a kernel read or write past an
+    allocation), or sits on another device than ``like``."""
+    if t is None:
+        if required:
+            raise ValueError(f"{name} is required")
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype not in dtypes:
+        names = ", ".join(str(d) for d in dtypes)
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {names}")
+    if like is not None and t.device != like.device:
+        raise ValueError(f"{name} is on {t.device}, q on {like.device}")
+
+
+def _check_attention(q, k, v, q_scale, k_scale, out, lse):
+    """Shapes and dtypes of the forward's tensors, all implied by q."""
+    import torch
+    if q.dim() != 4:
+        raise ValueError(f"q must be [batch, heads, seq_len, head_dim], got shape {tuple(q.shape)}")
+    _dtype_code(q)
+    b, h, n, d = q.shape
+    _expect(k, "k", q.shape, (q.dtype,), q)
+    vtype = torch.float32 if q.dtype == torch.float32 else torch.bfloat16
+    _expect(v, "v", q.shape, (vtype,), q)
+    _expect(out, "out", q.shape, (vtype,), q, required=False)
+    _expect(lse, "lse", (b, h, n), (torch.float32,), q, required=False)
+    scaled = q.dtype in (torch.int8, torch.uint8)
+    for name, s in (("q_scale", q_scale), ("k_scale", k_scale)):
+        if scaled:
+            _expect(s, name, (b, h, n), (torch.float32,), q)
+        elif s is not None:
+            raise ValueError(f"{name} is only for int8 / fp8 q and k")
+
+
+def _check_rows(x, codes, scales, code_dtype):
+    import torch
+    if x.dim() < 1:
+        raise ValueError("x must have at least one dimension")
+    _expect(x, "x", x.shape, (torch.float32,))
+    _expect(codes, "codes", x.shape, (code_dtype,), x, required=False)
+    _expect(scales, "scales", x.shape[:-1], (torch.float32,), x, required=False)
+
+
 def make_problem(q, *, causal: bool, p_bf16: bool = True, softmax_scale: float = 0.0,
                  dtype: Optional[int] = None, beta: Optional[float] = None) -> AttnProblem:
     """beta (> 1) selects the stabilised flash variant; None the standard one."""
@@ -184,6 +232,7 @@ def attn_fwd_flash(q, k, v, *, causal: bool, p_bf16: bool = True, softmax_scale:
     beta (> 1, bf16 inputs only) runs the stabilised variant, whose
     normaliser is beta*r_m (r_m > 0) or 0 (r_m < 0) when the row max r_m
     occurs more than once."""
+    _check_attention(q, k, v, q_scale, k_scale, out, lse)
     _contig(q, k, v, q_scale, k_scale, out, lse)
     out = _out_like(q, v) if out is None else out
     prob = make_problem(q, causal=causal, p_bf16=p_bf16, softmax_scale=softmax_scale, beta=beta)
@@ -196,6 +245,10 @@ def attn_fwd_flash_debug_s(q, k, v, *, causal: bool, p_bf16: bool = True,
                            softmax_scale: float = 0.0, q_scale=None, k_scale=None, out=None,
                            s_out=None, stream=None):
     """Int8 flash forward that also writes its int32 score tiles to s_out."""
+    import torch
+    _check_attention(q, k, v, q_scale, k_scale, out, None)
+    b, h, n, _ = q.shape
+    _expect(s_out, "s_out", (b, h, n, n), (torch.int32,), q)
     _contig(q, k, v, q_scale, k_scale, out, s_out)
     out = _out_like(q, v) if out is None else out
     prob = make_problem(q, causal=causal, p_bf16=p_bf16, softmax_scale=softmax_scale)
@@ -215,6 +268,9 @@ def attn_fwd_baseline(q, k, v, *, causal: bool, p_bf16: bool = True, softmax_sca
                       q_scale=None, k_scale=None, workspace=None, out=None, stream=None):
     """Baseline attention (S and P in the workspace); returns (out, workspace)."""
     import torch
+    _check_attention(q, k, v, q_scale, k_scale, out, None)
+    if workspace is not None and workspace.device != q.device:
+        raise ValueError(f"workspace is on {workspace.device}, q on {q.device}")
     _contig(q, k, v, q_scale, k_scale, out, workspace)
     out = _out_like(q, v) if out is None else out
     prob = make_problem(q, causal=causal, p_bf16=p_bf16, softmax_scale=softmax_scale)
@@ -237,12 +293,16 @@ def attn_deviation_scratch_size(n: int) -> int:
 def attn_deviation(o_test, o_ref, *, scratch=None, stream=None) -> dict:
     """Deviation summary of o_test (fp32/bf16) against o_ref (fp64), on the GPU."""
     import torch
-    _contig(o_test, o_ref, scratch)
+    if o_test.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError(f"o_test has dtype {o_test.dtype}, expected float32 or bfloat16")
     if o_ref.dtype != torch.float64:
         raise TypeError("o_ref must be float64")
     n = o_test.numel()
     if o_ref.numel() != n:
         raise ValueError("o_test and o_ref differ in size")
+    if o_ref.device != o_test.device or (scratch is not None and scratch.device != o_test.device):
+        raise ValueError("o_test, o_ref and scratch must be on one device")
+    _contig(o_test, o_ref, scratch)
     need = attn_deviation_scratch_size(n)
     if scratch is None:
         scratch = torch.empty(max(need, 1), dtype=torch.uint8, device=o_test.device)
@@ -256,9 +316,8 @@ def attn_deviation(o_test, o_ref, *, scratch=None, stream=None) -> dict:
 def attn_quantize_int8(x, *, codes=None, scales=None, stream=None):
     """Per-row int8 quantisation of fp32 x[..., d]; returns (codes, scales)."""
     import torch
+    _check_rows(x, codes, scales, torch.int8)
     _contig(x, codes, scales)
-    if x.dtype != torch.float32:
-        raise TypeError("x must be float32")
     d = x.shape[-1]
     rows = x.numel() // d if d else 0
     codes = torch.empty(x.shape, dtype=torch.int8, device=x.device) if codes is None else codes
@@ -273,9 +332,10 @@ def attn_quantize_int8_tiles(x, tile_rows: int, *, codes=None, scales=None, stre
     """Per-tile int8 quantisation of fp32 x[..., n, d] (tiles of tile_rows
     rows inside each leading index); returns (codes, per-row scales)."""
     import torch
+    if x.dim() < 2:
+        raise ValueError("x must be [..., n, d]")
+    _check_rows(x, codes, scales, torch.int8)
     _contig(x, codes, scales)
-    if x.dtype != torch.float32 or x.dim() < 2:
-        raise TypeError("x must be float32 [..., n, d]")
     n, d = x.shape[-2], x.shape[-1]
     groups = x.numel() // (n * d) if n * d else 0
     codes = torch.empty(x.shape, dtype=torch.int8, device=x.device) if codes is None else codes
@@ -290,9 +350,8 @@ def attn_quantize_fp8(x, *, codes=None, scales=None, stream=None):
     """Per-row E4M3 fp8 quantisation of fp32 x[..., d]; returns (codes as
     uint8 bytes, scales)."""
     import torch
+    _check_rows(x, codes, scales, torch.uint8)
     _contig(x, codes, scales)
-    if x.dtype != torch.float32:
-        raise TypeError("x must be float32")
     d = x.shape[-1]
     rows = x.numel() // d if d else 0
     codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device) if codes is None else codes
@@ -306,10 +365,14 @@ def attn_quantize_fp8(x, *, codes=None, scales=None, stream=None):
 def attn_bwd_delta(o, d_o, *, delta=None, stream=None):
     """delta = rowsum(d_o * o) over the last axis ([B,H,N,d] -> [B,H,N] fp32)."""
     import torch
-    _contig(o, d_o, delta)
-    if o.shape != d_o.shape or o.dtype != d_o.dtype:
-        raise ValueError("o and d_o must have the same shape and dtype")
+    if o.dim() != 4:
+        raise ValueError(f"o must be [batch, heads, seq_len, head_dim], got {tuple(o.shape)}")
+    if o.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError(f"o has dtype {o.dtype}, expected float32 or bfloat16")
+    _expect(d_o, "d_o", o.shape, (o.dtype,), o)
     b, h, n, d = o.shape
+    _expect(delta, "delta", (b, h, n), (torch.float32,), o, required=False)
+    _contig(o, d_o, delta)
     delta = (torch.empty((b, h, n), dtype=torch.float32, device=o.device)
              if delta is None else delta)
     code = ATTN_F32 if o.dtype == torch.float32 else ATTN_BF16
@@ -330,11 +393,15 @@ def attn_wasserstein(a, b, *, scratch=None, stream=None) -> dict:
     """W1, W2 and W_inf between the value distributions of a and b (same
     number of elements; fp32, bf16 or fp64 each), on the GPU."""
     import torch
-    _contig(a, b, scratch)
     n = a.numel()
     if b.numel() != n:
         raise ValueError("a and b differ in size")
     ta, tb = _dtype_code(a), _dtype_code(b)
+    if ATTN_INT8 in (ta, tb) or ATTN_FP8 in (ta, tb):
+        raise TypeError("a and b must be float32, bfloat16 or float64")
+    if b.device != a.device or (scratch is not None and scratch.device != a.device):
+        raise ValueError("a, b and scratch must be on one device")
+    _contig(a, b, scratch)
     need = attn_wasserstein_scratch_size(n, ta, tb)
     if scratch is None:
         scratch = torch.empty(max(need, 1), dtype=torch.uint8, device=a.device)
@@ -355,6 +422,16 @@ def attn_bwd_flash(q, k, v, o, d_o, lse, *, causal: bool, softmax_scale: float =
                    dq=None, dk=None, dv=None, workspace=None, stream=None):
     """FlashAttention backward (bf16); returns (dq, dk, dv)."""
     import torch
+    if q.dim() != 4:
+        raise ValueError(f"q must be [batch, heads, seq_len, head_dim], got {tuple(q.shape)}")
+    if q.dtype != torch.bfloat16:
+        raise TypeError(f"q has dtype {q.dtype}; the backward is built for bfloat16")
+    b, h, n, _ = q.shape
+    for name, t in (("k", k), ("v", v), ("o", o), ("d_o", d_o)):
+        _expect(t, name, q.shape, (torch.bfloat16,), q)
+    _expect(lse, "lse", (b, h, n), (torch.float32,), q)
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _expect(t, name, q.shape, (torch.bfloat16,), q, required=False)
     _contig(q, k, v, o, d_o, lse, dq, dk, dv, workspace)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
@@ -368,6 +445,36 @@ def attn_bwd_flash(q, k, v, o, d_o, lse, *, causal: bool, softmax_scale: float =
                                  _ptr(workspace), workspace.numel() * workspace.element_size(),
                                  _stream(stream)))
     return dq, dk, dv
+
+
+def attn_clock_sample(out, *, stream=None):
+    """Enqueue one clock sample per row of ``out`` (an int64 [slots, 3]
+    CUDA tensor): (location, shader-clock counter, 100 MHz counter)."""
+    import torch
+    if out.dim() != 2 or out.shape[1] != 3 or out.dtype != torch.int64:
+        raise ValueError("out must be an int64 [slots, 3] tensor")
+    _contig(out)
+    _check(load().attn_clock_sample(_ptr(out), out.shape[0], _stream(stream)))
+    return out
+
+
+def shader_clock_mhz(before, after) -> Optional[float]:
+    """Average shader clock between two clock samples (host arrays of
+    [slots, 3]), compared on each location (CU) found in both; None when
+    there is none."""
+    first = {}
+    for row in before:
+        first.setdefault(int(row[0]), row)
+    rates = []
+    done = set()
+    for row in after:
+        loc = int(row[0])
+        if loc in first and loc not in done:
+            done.add(loc)
+            dr = int(row[2]) - int(first[loc][2])
+            if dr > 0:
+                rates.append(100.0 * (int(row[1]) - int(first[loc][1])) / dr)
+    return sum(rates) / len(rates) if rates else None
 
 
 def attn_version() -> str:

@@ -318,6 +318,13 @@ attn_status_t attn_deviation(const void* o_test, int32_t o_dtype, const double* 
   return ok();
 }
 
+attn_status_t attn_clock_sample(uint64_t* out, int32_t slots, void* stream) {
+  if (slots < 1 || slots > 4096) return fail(ATTN_ERR_INVALID_ARG, "slots must be in [1, 4096]");
+  if (out == nullptr) return fail(ATTN_ERR_INVALID_ARG, "out is NULL");
+  return from_hip(pn::launch_clock_sample(out, slots, (hipStream_t)stream),
+                  "attn_clock_sample launch");
+}
+
 static bool w_dtype_ok(int32_t t) { return t == ATTN_F32 || t == ATTN_BF16 || t == ATTN_F64; }
 
 attn_status_t attn_wasserstein_scratch_size(int64_t n, int32_t a_dtype, int32_t b_dtype,

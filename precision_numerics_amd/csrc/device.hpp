@@ -118,4 +118,29 @@ __device__ __forceinline__ uint8_t f32_to_e4m3(float x) {
   return (uint8_t)(sign | mag);
 }
 
+// Compile-time constants as types, for loops whose index must be a constant.
+template <int I> struct IntC { static constexpr int value = I; };
+template <bool B> struct BoolC { static constexpr bool value = B; };
+
+// f(IntC<0>{}), ..., f(IntC<N-1>{}): a loop whose index is a constant
+template <int N, int I = 0, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(IntC<I>{});
+    static_for<N, I + 1>(f);
+  }
+}
+
+// Row order of a 32-row MFMA A operand that makes the 32x32 accumulator
+// land in the order of the next product's operand: when row m of the A
+// operand carries element perm_row(m) of its 32-element subtile, accumulator
+// register r of lane group g (lanes 32g..32g+31) holds element
+// elem_of_reg(r, g) = 16(r/8) + 8g + r%8, so a lane's sixteen results of a
+// subtile are, in register order, the sixteen consecutive pairs of eight
+// elements that lane feeds as the B operand of a 32x32x16 product.
+__device__ __forceinline__ int perm_row(int m) {
+  return 16 * (m >> 4) + 8 * ((m >> 2) & 1) + 4 * ((m >> 3) & 1) + (m & 3);
+}
+__device__ __forceinline__ int elem_of_reg(int r, int g) { return 16 * (r >> 3) + 8 * g + (r & 7); }
+
 }  // namespace pn

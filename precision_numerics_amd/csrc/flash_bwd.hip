@@ -63,13 +63,6 @@ struct BwdParams {
   float scale_log2;   // scale * log2(e)
 };
 
-// Row m of a 32-row A operand carries element perm_row(m) of its subtile;
-// then accumulator register r of lane group g holds element elem_of_reg(r, g).
-__device__ __forceinline__ int perm_row(int m) {
-  return 16 * (m >> 4) + 8 * ((m >> 2) & 1) + 4 * ((m >> 3) & 1) + (m & 3);
-}
-__device__ __forceinline__ int elem_of_reg(int r, int g) { return 16 * (r >> 3) + 8 * g + (r & 7); }
-
 // Workgroup -> (head, tile).  Workgroups go to the eight XCDs in turn, so
 // heads are taken in groups of eight, head 8c + x on XCD x: each XCD then
 // works through its heads one at a time, all tiles of a head together, and
@@ -127,18 +120,6 @@ template <int D> __device__ __forceinline__ uint32_t swz_src_offset(int seg, int
   return (uint32_t)(R * kRow + 16 * (cpos ^ swz<D>(R)));
 }
 
-template <int I> struct Slot { static constexpr int value = I; };
-template <bool B> struct Flag { static constexpr bool value = B; };
-
-// f(Slot<0>{}), ..., f(Slot<N-1>{}): a loop whose index is a constant
-template <int N, int I = 0, typename F>
-__device__ __forceinline__ void for_slots(F&& f) {
-  if constexpr (I < N) {
-    f(Slot<I>{});
-    for_slots<N, I + 1>(f);
-  }
-}
-
 // This wave's share of the buffer-to-LDS loads that fill the LDS image of a
 // STEP-row block of a [N][D] bf16 matrix, among W issuing waves: segments
 // w, w + W, .., with each lane's source offset inside the block (rows past N
@@ -158,7 +139,7 @@ template <int D, int STEP, int W> struct BlockDma {
   // rows r0.. into the block image at LDS address lds
   __device__ __forceinline__ void issue(i32x4 rs, int r0, uint32_t lds) const {
     const uint32_t soff = (uint32_t)r0 * G::kRow;
-    for_slots<kPer>([&](auto ic) __attribute__((always_inline)) {
+    static_for<kPer>([&](auto ic) __attribute__((always_inline)) {
       constexpr int i = decltype(ic)::value;
       if (W * i + W - 1 < G::kSeg || wave + W * i < G::kSeg)
         lds_load16<i * W * 1024>(rs, off[i], soff, lds + wave * 1024);
@@ -330,11 +311,11 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p) {
   int kb = 0, buf = 0;
   for (; kb < kfull; kb += kStep, buf ^= 1) {
     stage(kb, buf);
-    step(kb, buf, Flag<false>{});
+    step(kb, buf, BoolC<false>{});
   }
   for (; kb < kend; kb += kStep, buf ^= 1) {
     stage(kb, buf);
-    step(kb, buf, Flag<true>{});
+    step(kb, buf, BoolC<true>{});
   }
   if (qok) store_row<D>(p.dq + hoff + (int64_t)qrow * D, dq, p.scale, g);
 }
@@ -449,7 +430,7 @@ __global__ __launch_bounds__(64 * kDkvWaves, 2) void bwd_dkv_kernel(BwdParams p)
     for (int t = 0; t < QST; ++t) a[t] = *(const i32x4*)(ar + la.row[t]);
     __builtin_amdgcn_sched_barrier(0);
     f32x16 sd = f32x16{};
-    for_slots<QST>([&](auto tc) __attribute__((always_inline)) {
+    static_for<QST>([&](auto tc) __attribute__((always_inline)) {
       constexpr int t = decltype(tc)::value;
       sd = mfma_bf16(__builtin_bit_cast(bf16x8, a[t]), __builtin_bit_cast(bf16x8, kr[t]), sd);
       // 2 DT transposing read pairs over QST = 2 DT products
@@ -525,11 +506,11 @@ __global__ __launch_bounds__(64 * kDkvWaves, 2) void bwd_dkv_kernel(BwdParams p)
   const int jmask = CAUSAL ? min(nblk, kDkvTile / kStep) : 0;
   const int jfull = min(nblk, max(jmask, (N - qstart) / kStep));
   issue(qstart, 0);
-  step(Flag<true>{}, Slot<1>{});
-  while (j < jmask) step(Flag<true>{}, Slot<0>{});
-  while (j < jfull) step(Flag<false>{}, Slot<0>{});
-  while (j < nblk) step(Flag<true>{}, Slot<0>{});
-  step(Flag<false>{}, Slot<2>{});
+  step(BoolC<true>{}, IntC<1>{});
+  while (j < jmask) step(BoolC<true>{}, IntC<0>{});
+  while (j < jfull) step(BoolC<false>{}, IntC<0>{});
+  while (j < nblk) step(BoolC<true>{}, IntC<0>{});
+  step(BoolC<false>{}, IntC<2>{});
   if (kok) {
     if (role == 0)
       store_row<D>(p.dv + hoff + (int64_t)krow * D, acc, 1.0f, g);

@@ -23,10 +23,9 @@
 //  * The eight waves form two groups of four, one wave of each group per
 //    SIMD.  The groups run half a step apart, so that while one wave of a
 //    SIMD issues its matrix products (P_{j-1} V_{j-1}, then S_j) the other
-//    does its softmax arithmetic (mask, max, exp, sums) on VALU: the two
-//    instruction streams overlap on each SIMD.  The rescale of O by
-//    exp(m - m') is issued in the matrix half-step, in the shadow of the
-//    P V products, which keeps the two half-steps closer in length.
+//    does its softmax arithmetic (mask, max, exp, sums, the rescale of O by
+//    exp(m - m'), P -> bf16) on VALU: the two instruction streams overlap
+//    on each SIMD, and the matrix half-step holds no VALU instruction.
 //  * The wave computes S^T = K_j Q^T (32 keys x 32 queries per MFMA tile), so
 //    lane l owns query l%32 and half of the block's keys: the row max and row
 //    sum are in-lane reductions plus one permlane32_swap, and exp(m - m') is
@@ -42,9 +41,11 @@
 //    v_exp_f32 per score.  At the row max the fma leaves only the rounding
 //    residual of the scaled max, so P is 1 to within an ulp there and exactly
 //    1 once rounded to bf16.
-//  * Grid = (batch*heads, query tiles).  Causal launches hand out the longest
-//    query tiles first; when batch*heads is a multiple of 8 all tiles of one
-//    head land on the same XCD (round-robin dispatch), sharing its L2.
+//  * Persistent grid: min(tiles, compute units) workgroups, each walking a
+//    list of 256-row query tiles (see tile_of): every tile of a head runs on
+//    one XCD, causal launches hand out the longest tiles first, and the
+//    next tile's first K/V block and Q rows load while the current tile
+//    finishes.
 #include "device.hpp"
 #include "launch.hpp"
 #include "lds_dma.hpp"
@@ -60,6 +61,9 @@ template <int QK> constexpr bool kScaledQK = QK == QK_I8 || QK == QK_F8;
 enum PVKind { PV_BF16 = 0, PV_F32_VBF16 = 1, PV_F32_VF32 = 2 };
 
 constexpr int kWaves = 8;            // two groups of four: one wave of each per SIMD
+// Stabilised variant: largest distance (log2 units) of the normaliser above
+// the running row max (see the range guard in the softmax half-step).
+constexpr float kStabMaxShift = 64.f;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBR = 32 * kWaves;     // query rows per workgroup
 
@@ -172,15 +176,6 @@ __device__ __forceinline__ TileId tile_of(const FlashParams& p, int round) {
   return t;
 }
 
-// Key (0..31 inside a 32-key subtile) that row m of the K operand carries.
-__device__ __forceinline__ int key_of_row(int m) {
-  return 16 * (m >> 4) + 8 * ((m >> 2) & 1) + 4 * ((m >> 3) & 1) + (m & 3);
-}
-// Key (0..31 inside a 32-key subtile) in accumulator register r of group g.
-__device__ __forceinline__ int key_of_reg(int r, int g) {
-  return 16 * (r >> 3) + 8 * g + (r & 7);
-}
-
 // Max of the N scores of a lane as a tree of 3-input maxima (v_max3_f32).
 template <int N>
 __device__ __forceinline__ float tree_max(const float (&x)[N]) {
@@ -196,18 +191,6 @@ __device__ __forceinline__ float tree_max(const float (&x)[N]) {
     if constexpr (N % 3 == 1) y[M - 1] = x[N - 1];
     if constexpr (N % 3 == 2) y[M - 1] = fmaxf(x[N - 2], x[N - 1]);
     return tree_max<M>(y);
-  }
-}
-
-template <bool B> struct BoolC { static constexpr bool value = B; };
-template <int I> struct IntC { static constexpr int value = I; };
-
-// f(IntC<0>{}), ..., f(IntC<N-1>{}): a loop whose index is a constant
-template <int N, int I = 0, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (I < N) {
-    f(IntC<I>{});
-    static_for<N, I + 1>(f);
   }
 }
 
@@ -449,7 +432,7 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
     for (int r = 0; r < 16; ++r) s[ks][r] = 0.f;
 
   // per-lane LDS byte offsets of the operand reads (block-independent)
-  const int k_lane = key_of_row(n) * TL::kStrK;
+  const int k_lane = perm_row(n) * TL::kStrK;
   const int v_lane = (8 * g + ((lane & 15) >> 2)) * TL::kStrV +
                      (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * (int)sizeof(VT);
 
@@ -459,8 +442,7 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
   // (in this order the P_{j-1} registers die before the new scores are born).
   // DO_PV / DO_S select the parts at compile time, so that the steady-state
   // step is one straight-line region the scheduler can interleave: LDS reads
-  // run a few matrix products ahead of their use, and the rescale of O is
-  // spread over the products of the preceding d subtile.
+  // run a few matrix products ahead of their use.
   // Loads a matrix half-step issues for a following block (of this tile or
   // of the next one): rows kb.. of the K (group 0) or V (group 1) head at
   // base (and, for int8 K, its key scales at sbase) into buffer buf, if on.
@@ -624,7 +606,7 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
           for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-              const VT* vr = (const VT*)(vt + (32 * ks + key_of_reg(r, g)) * TL::kStrV) + n;
+              const VT* vr = (const VT*)(vt + (32 * ks + elem_of_reg(r, g)) * TL::kStrV) + n;
 #pragma unroll
               for (int dt = 0; dt < DT; ++dt)
                 oacc[dt] = mfma_f32(to_f32<VT>(vr[32 * dt]), pf[ks][r], oacc[dt]);
@@ -682,7 +664,7 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
                 int32_t* dst = p.s_dbg + ((int64_t)bh * N + qrow) * (int64_t)N;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                  const int key = jl * BC + 32 * ks + key_of_reg(r, g);
+                  const int key = jl * BC + 32 * ks + elem_of_reg(r, g);
                   if (key < N) dst[key] = acc[r];
                 }
               }
@@ -690,7 +672,7 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
             // exact int32 -> fp32 (|acc| < 2^24), then the per-row scales
 #pragma unroll
             for (int r = 0; r < 16; ++r)
-              s[ks][r] = (float)acc[r] * (skt[32 * ks + key_of_reg(r, g)] * sq_log2);
+              s[ks][r] = (float)acc[r] * (skt[32 * ks + elem_of_reg(r, g)] * sq_log2);
           }
         } else if constexpr (QK == QK_F8) {
           // E4M3 codes in the int8 layout: two fp8 products per 32-byte
@@ -705,7 +687,7 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
               acc = mfma_fp8x2(*(const i32x4*)(krow + 32 * st), qv[st], acc);
 #pragma unroll
             for (int r = 0; r < 16; ++r)
-              s[ks][r] = acc[r] * (skt[32 * ks + key_of_reg(r, g)] * sq_log2);
+              s[ks][r] = acc[r] * (skt[32 * ks + elem_of_reg(r, g)] * sq_log2);
           }
         } else {
 #pragma unroll
@@ -792,8 +774,16 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
       cnt = pair32_isum(cnt);
       nmax_run = (mx > mraw_run) ? cnt : (mx == mraw_run ? nmax_run + cnt : nmax_run);
       if (nmax_run >= 2) {
+        const float m_max = m_use;  // the running max in log2 units
         if (mraw_new > 0.f) m_use *= p.beta;
         else if (mraw_new < 0.f) m_use = 0.f;
+        // Range guard: the page's rule puts the normaliser (beta-1)|r_m|
+        // (r_m > 0) or |r_m| (r_m < 0) above the row max, which for large
+        // |r_m| underflows every exp2 in fp32 and leaves l = 0, O = 0/0.
+        // The shift is capped at kStabMaxShift, so the largest P stays at
+        // or above 2^-kStabMaxShift (still below 1, as the variant wants);
+        // inside the cap the rule applies unchanged.
+        m_use = fminf(m_use, m_max + kStabMaxShift);
       }
     }
     mraw_run = mraw_new;

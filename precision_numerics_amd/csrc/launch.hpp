@@ -89,4 +89,8 @@ hipError_t launch_quantize_tiles(const float* x, int64_t groups, int64_t n, int6
 hipError_t launch_quantize_fp8(const float* x, int64_t rows, int64_t d,
                                uint8_t* codes, float* scales, hipStream_t stream);
 
+// One workgroup per slot records (XCD id, shader-clock counter, 100 MHz
+// counter) into out[3 * slot + 0..2].
+hipError_t launch_clock_sample(uint64_t* out, int slots, hipStream_t stream);
+
 }  // namespace pn

@@ -156,6 +156,7 @@ def test_repeated_max_closed_form(lib, sign):
     stb = out_to_f64(o_stb)[0, 0, :, 0]
     exp_std = _expected_col0(q, k, v, r, scale)
     m_stab = beta * r if r > 0 else (0.0 if r < 0 else r)
+    assert m_stab - r < MAX_SHIFT_NAT          # inside the range guard
     exp_stb = _expected_col0(q, k, v, m_stab, scale)
     _print(f"sign={sign}: standard {std[0]!r} (expected {exp_std!r}), "
            f"stabilized {stb[0]!r} (expected {exp_stb!r})")
@@ -166,3 +167,63 @@ def test_repeated_max_closed_form(lib, sign):
     else:
         assert abs(exp_stb) > 1e-3
         assert np.all(np.abs(stb - exp_stb) <= 4e-3 * abs(exp_stb) + 1e-7)
+
+
+# the kernel's range guard: the normaliser stays within 64 (log2 units) of
+# the running row max
+MAX_SHIFT_NAT = 64.0 * np.log(2.0)
+
+
+def _far_tie_case(sign: int, d=64, n=40):
+    """A repeated row maximum far from 0: r_m = 60.5 (sign > 0; beta = 4 puts
+    the page's normaliser 181.5 above it) or r_m = -120 (sign < 0; the
+    normaliser 0 is 120 above it).  Either way every exp of the unguarded
+    rule underflows in fp32.  Keys 0 and 8 carry the maximum, every other key
+    scores at least 60 lower, so the exact output of every row is the mean
+    of V rows 0 and 8 (to within e^-60)."""
+    q = np.zeros((1, 1, n, d), np.float32)
+    k = np.zeros((1, 1, n, d), np.float32)
+    v = np.zeros((1, 1, n, d), np.float32)
+    rest = [i for i in range(n) if i not in (0, 8)]
+    if sign > 0:
+        q[..., 0] = 22.0
+        k[:, :, [0, 8], 0] = 22.0          # dot 484 -> scaled 60.5
+    else:
+        q[..., 0] = -32.0
+        k[:, :, [0, 8], 0] = 30.0          # dot -960 -> scaled -120
+        k[:, :, rest, 0] = 60.0            # dot -1920 -> -240
+    v[:, :, :, :] = np.arange(d, dtype=np.float32) / 8.0 - 3.0
+    v[:, :, 0, :] = 1.5
+    v[:, :, 8, :] = -0.25                  # mean of rows 0 and 8: 0.625
+    v[:, :, rest, 1] = 100.0               # weight e^-60 or less: invisible
+    return q, k, v
+
+
+@pytest.mark.parametrize("sign", [1, -1])
+@pytest.mark.parametrize("p_bf16", [True, False])
+def test_range_guard_keeps_far_repeated_max_finite(lib, sign, p_bf16):
+    """The page's rule alone would give O = 0/0 here; with the guard the
+    largest probability is 2^-64 (exactly, after the bf16 rounding of P) and
+    the output is the exact softmax's: the mean of V rows 0 and 8, as the
+    FP64 oracle and the standard kernel give."""
+    beta = 4.0
+    q, k, v = _far_tie_case(sign)
+    scale = 1.0 / 8.0
+    s = scale * (k[0, 0] @ q[0, 0, 0])
+    r = float(s.max())
+    assert (s == r).sum() == 2 and np.sort(s)[-3] <= r - 60
+    m_rule = beta * r if r > 0 else 0.0
+    assert (m_rule - r) * np.log2(np.e) > 149      # fp32 exp2 underflows everywhere
+    tq, tk, tv = (torch_bf16(synth.f32_to_bf16_bits(x)) for x in (q, k, v))
+    o_std, _ = _forward(tq, tk, tv, None, p_bf16=p_bf16)
+    o_stb, lse = _forward(tq, tk, tv, beta, p_bf16=p_bf16, lse=True)
+    ref, lse_ref = oracle.attention(*(x.astype(np.float64) for x in (q, k, v)), causal=False)
+    stb, std = out_to_f64(o_stb), out_to_f64(o_std)
+    _print(f"sign={sign} p_bf16={p_bf16}: r_m={r} stabilized O[0,:4]={stb[0, 0, 0, :4]} "
+           f"ref={ref[0, 0, 0, :4]}")
+    assert np.all(np.isfinite(stb))
+    want = 0.5 * (v[0, 0, 0] + v[0, 0, 8]).astype(np.float64)
+    assert np.array_equal(stb[0, 0], np.broadcast_to(want, stb[0, 0].shape))
+    assert np.array_equal(std, stb)
+    assert np.abs(ref - want).max() <= 1e-12
+    assert np.abs(lse.cpu().numpy().astype(np.float64) - lse_ref).max() <= 1e-4 * abs(r)
