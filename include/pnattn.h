@@ -177,6 +177,22 @@ attn_status_t attn_deviation(const void* o_test, int32_t o_dtype,
                              size_t scratch_bytes, attn_deviation_t* out_host,
                              void* stream);
 
+/* attn_deviation without a caller-provided scratch buffer, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight
+ * serving or training loops, harnesses that forbid allocation).  The
+ * partial sums live in a 64 KiB device array of the library, one per GPU,
+ * located on the first call on each device and held until the process
+ * ends; the call itself allocates nothing (no hipMalloc, no library
+ * allocation).  The array holds the scratch of every n >= 0 (the partials
+ * are capped at 1024 records); a size whose scratch would not fit is
+ * rejected with ATTN_ERR_WORKSPACE.  Every call on one GPU uses that GPU's
+ * array: calls that overlap on one GPU (other host threads, other streams)
+ * race and must not be issued.  Same arguments, statistics and bitwise
+ * results as attn_deviation; synchronises its stream before it returns. */
+attn_status_t attn_deviation_noalloc(const void* o_test, int32_t o_dtype,
+                                     const double* o_ref, int64_t n,
+                                     attn_deviation_t* out_host, void* stream);
+
 /* Wasserstein distances between the empirical distributions of two tensors
  * of n values each ("Is Flash Attention Stable?", abstract: the impact of
  * numeric deviation measured with the Wasserstein distance, after

@@ -81,6 +81,8 @@ _SIGNATURES = {
     "attn_deviation_scratch_size": [ctypes.c_int64, ctypes.POINTER(ctypes.c_size_t)],
     "attn_deviation": [_P, ctypes.c_int32, _P, ctypes.c_int64, _P, ctypes.c_size_t,
                        ctypes.POINTER(AttnDeviation), _P],
+    "attn_deviation_noalloc": [_P, ctypes.c_int32, _P, ctypes.c_int64,
+                               ctypes.POINTER(AttnDeviation), _P],
     "attn_quantize_int8": [_P, ctypes.c_int64, ctypes.c_int64, _P, _P, _P],
     "attn_quantize_fp8": [_P, ctypes.c_int64, ctypes.c_int64, _P, _P, _P],
     "attn_quantize_int8_tiles": [_P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
@@ -310,6 +312,25 @@ def attn_deviation(o_test, o_ref, *, scratch=None, stream=None) -> dict:
     _check(load().attn_deviation(_ptr(o_test), _dtype_code(o_test), _ptr(o_ref), n, _ptr(scratch),
                                  scratch.numel() * scratch.element_size(), ctypes.byref(res),
                                  _stream(stream)))
+    return res.as_dict()
+
+
+def attn_deviation_noalloc(o_test, o_ref, *, stream=None) -> dict:
+    """attn_deviation with the library's own scratch array (no allocation)."""
+    import torch
+    if o_test.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError(f"o_test has dtype {o_test.dtype}, expected float32 or bfloat16")
+    if o_ref.dtype != torch.float64:
+        raise TypeError("o_ref must be float64")
+    n = o_test.numel()
+    if o_ref.numel() != n:
+        raise ValueError("o_test and o_ref differ in size")
+    if o_ref.device != o_test.device:
+        raise ValueError("o_test and o_ref must be on one device")
+    _contig(o_test, o_ref)
+    res = AttnDeviation()
+    _check(load().attn_deviation_noalloc(_ptr(o_test), _dtype_code(o_test), _ptr(o_ref), n,
+                                         ctypes.byref(res), _stream(stream)))
     return res.as_dict()
 
 

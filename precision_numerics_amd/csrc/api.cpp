@@ -318,6 +318,29 @@ attn_status_t attn_deviation(const void* o_test, int32_t o_dtype, const double* 
   return ok();
 }
 
+attn_status_t attn_deviation_noalloc(const void* o_test, int32_t o_dtype, const double* o_ref,
+                                     int64_t n, attn_deviation_t* out_host, void* stream) {
+  if (out_host == nullptr) return fail(ATTN_ERR_INVALID_ARG, "out_host is NULL");
+  if (n < 0) return fail(ATTN_ERR_INVALID_ARG, "n must be >= 0");
+  if (o_dtype != ATTN_F32 && o_dtype != ATTN_BF16)
+    return fail(ATTN_ERR_INVALID_ARG, "o_dtype must be ATTN_F32 or ATTN_BF16");
+  if (n == 0) {
+    *out_host = attn_deviation_t{0, 0, 0, 0, 0, 0, 0, 0, -1};
+    return ok();
+  }
+  if (o_test == nullptr || o_ref == nullptr)
+    return fail(ATTN_ERR_INVALID_ARG, "o_test and o_ref must be non-NULL");
+  const size_t need = pn::deviation_scratch_bytes(n);
+  const size_t have = pn::deviation_noalloc_capacity();
+  if (need > have)
+    return fail(ATTN_ERR_WORKSPACE, "n = %lld needs %zu bytes of scratch; the library's own "
+                "array holds %zu", (long long)n, need, have);
+  void* scratch = nullptr;
+  hipError_t e = pn::deviation_noalloc_scratch(&scratch);
+  if (e != hipSuccess) return from_hip(e, "attn_deviation_noalloc: locating the scratch array");
+  return attn_deviation(o_test, o_dtype, o_ref, n, scratch, have, out_host, stream);
+}
+
 attn_status_t attn_clock_sample(uint64_t* out, int32_t slots, void* stream) {
   if (slots < 1 || slots > 4096) return fail(ATTN_ERR_INVALID_ARG, "slots must be in [1, 4096]");
   if (out == nullptr) return fail(ATTN_ERR_INVALID_ARG, "out is NULL");

@@ -8,6 +8,8 @@
 //   pass 1: G workgroups, each over one contiguous chunk, write a partial
 //   pass 2: one workgroup folds the G partials in index order
 // HBM-bound: reads n * (2 or 4) bytes of o_test and 8n bytes of o_ref once.
+#include <mutex>
+
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -113,10 +115,40 @@ int blocks_for(int64_t n) {
   return (int)b;
 }
 
+// Scratch of the allocation-free entry point: one array per GPU, held until
+// the process ends.  Its size covers the largest scratch any n needs (the
+// partials are capped at kMaxBlocks).  In host code `scratch` names a
+// host-side stand-in, not device memory: only the address returned by
+// hipGetSymbolAddress for the current device may be passed to kernels.
+constexpr size_t kNoAllocScratchBytes = 64 * 1024;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
 }  // namespace
 
 size_t deviation_scratch_bytes(int64_t n) {
   return (size_t)blocks_for(n) * sizeof(Partial) + sizeof(DeviationRecord) + 256;
+}
+
+size_t deviation_noalloc_capacity() { return kNoAllocScratchBytes; }
+
+hipError_t deviation_noalloc_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_deviation(const void* o_test, int o_dtype, const double* o_ref, int64_t n,

@@ -45,6 +45,10 @@ struct DeviationRecord {
 hipError_t launch_deviation(const void* o_test, int o_dtype,
                             const double* o_ref, int64_t n, void* scratch,
                             DeviationRecord* out_host, hipStream_t stream);
+// The library's own deviation scratch on the current device (a file-scope
+// device array, located once per device): its device address and size.
+hipError_t deviation_noalloc_scratch(void** ptr);
+size_t deviation_noalloc_capacity();
 
 // FlashAttention backward (bf16): delta = rowsum(dO o O) into `delta`
 // (B*H*N fp32, caller's workspace), then dK/dV and dQ.

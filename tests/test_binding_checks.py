@@ -159,7 +159,7 @@ def test_wasserstein_checks():
         pna.attn_wasserstein(t(10, torch.int8), t(10, f32))
 
 
-@pytest.mark.parametrize("call", ["wasserstein", "deviation", "delta",
+@pytest.mark.parametrize("call", ["wasserstein", "deviation", "deviation_noalloc", "delta",
                                   "quant", "tiles", "fp8", "baseline", "backward", "debug_s"])
 def test_well_formed_calls_reach_the_device_check(call):
     """Every binding function runs its checks to the end on well-formed CPU
@@ -169,6 +169,8 @@ def test_well_formed_calls_reach_the_device_check(call):
     calls = {
         "wasserstein": lambda: pna.attn_wasserstein(t(10, f32), t(10, torch.float64)),
         "deviation": lambda: pna.attn_deviation(t(10, f32), t(10, torch.float64)),
+        "deviation_noalloc": lambda: pna.attn_deviation_noalloc(t(10, bf16),
+                                                                t(10, torch.float64)),
         "delta": lambda: pna.attn_bwd_delta(q, q.clone()),
         "quant": lambda: pna.attn_quantize_int8(t((5, 64), f32)),
         "tiles": lambda: pna.attn_quantize_int8_tiles(t((2, 5, 64), f32), 2),
