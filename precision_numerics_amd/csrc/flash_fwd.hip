@@ -46,6 +46,8 @@
 //    one XCD, causal launches hand out the longest tiles first, and the
 //    next tile's first K/V block and Q rows load while the current tile
 //    finishes.
+#include <atomic>
+
 #include "device.hpp"
 #include "launch.hpp"
 #include "lds_dma.hpp"
@@ -804,8 +806,14 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
         rsum[r & 3] += s[ks][r];
       }
     l_run = l_run * alpha + ((rsum[0] + rsum[1]) + (rsum[2] + rsum[3]));
+    // At d = 128, exp(m - m') is often exactly 1 on every lane of a wave
+    // late in long rows (no row max of the wave moved): multiplying by 1
+    // changes no bit, so the rescale is skipped.  (At d = 64 the rows are
+    // short and the test costs more than it saves.)
+    if (D == 64 || __builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
+      for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
+    }
     if constexpr (PV == PV_BF16) {
 #pragma unroll
       for (int u = 0; u < BC / 16; ++u)
@@ -1038,6 +1046,25 @@ hipError_t launch_d(const AttnArgs& a, const FlashParams& fp, int64_t bh, int nt
   return hipErrorInvalidValue;
 }
 
+// Compute units of the current device, queried once per device.
+hipError_t compute_units(int* cus) {
+  constexpr int kMaxDev = 64;
+  static std::atomic<int> cache[kMaxDev];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev >= 0 && dev < kMaxDev) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) {
+      *cus = c;
+      return hipSuccess;
+    }
+  }
+  e = hipDeviceGetAttribute(cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e == hipSuccess && dev >= 0 && dev < kMaxDev) cache[dev].store(*cus, std::memory_order_relaxed);
+  return e;
+}
+
 }  // namespace
 
 hipError_t launch_flash(const AttnArgs& a, hipStream_t stream) {
@@ -1061,13 +1088,16 @@ hipError_t launch_flash(const AttnArgs& a, hipStream_t stream) {
   fp.tiles = bh * ntiles;
   // one workgroup per compute unit (the LDS footprint allows no second),
   // each walking its share of the tiles
-  int dev = 0, cus = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  int cus = 0;
+  hipError_t e = compute_units(&cus);
   if (e != hipSuccess) return e;
   fp.grid = (unsigned)(fp.tiles < (int64_t)cus ? fp.tiles : (int64_t)cus);
-  fp.grp4 = (bh % 32 == 0 && fp.grid % 8 == 0) ? 1 : 0;
+  // Four heads per XCD at a time keeps the re-read K/V rows of long causal
+  // sequences in L2; it needs at least two rounds of tiles.  With fewer, the
+  // global longest-first order, the second round dealt in reverse, gives every
+  // workgroup a balanced share (e.g. 1.5 rounds of 2/4/6/8-block tiles: at most
+  // 8 blocks per workgroup, against 10 in head groups).
+  fp.grp4 = (bh % 32 == 0 && fp.grid % 8 == 0 && fp.tiles >= 2 * (int64_t)fp.grid) ? 1 : 0;
   if (a.head_dim == 64) return launch_d<64>(a, fp, bh, ntiles, stream);
   if (a.head_dim == 128) return launch_d<128>(a, fp, bh, ntiles, stream);
   return hipErrorInvalidValue;
