@@ -308,7 +308,9 @@ def cpu_baseline_bias_refs(c4_inputs, workers):
 def bias_leg(pna, torch, refs, c4_inputs):
     """Rounding bias of standard versus stabilised FlashAttention: signed and
     absolute error against the FP64 references of the sampled heads, for P
-    rounded to bf16 and P kept in fp32."""
+    rounded to bf16 and P kept in fp32, with O stored in bf16 and in fp32 (the
+    fp32 O leaves out the rounding of O itself, so what remains is the
+    rounding upstream of it: P and the accumulation)."""
     cfg, qbits, variants = bias_inputs(c4_inputs)
     b, h, n, d = cfg.shape
 
@@ -321,15 +323,17 @@ def bias_leg(pna, torch, refs, c4_inputs):
         kt, vt = dev_bf16(kbits), dev_bf16(vbits)
         ref_t = torch.from_numpy(refs[name]).cuda()
         res = {}
-        for p_bf16 in (True, False):
-            row = {}
-            for kind, bb in (("standard", None), ("stabilized", BIAS_BETA)):
-                o = pna.attn_fwd_flash(q, kt, vt, causal=True, p_bf16=p_bf16, beta=bb)
-                o_s = torch.stack([o.view(b * h, n, d)[u] for u in BIAS_UNITS]).contiguous()
-                dev = pna.attn_deviation(o_s, ref_t)
-                row[kind] = {key: dev[key] for key in ("mean_signed", "mean_abs", "max_abs",
-                                                       "rms", "n_nonfinite")}
-            res["p_bf16" if p_bf16 else "p_fp32"] = row
+        for o_f32 in (False, True):
+            for p_bf16 in (True, False):
+                row = {}
+                for kind, bb in (("standard", None), ("stabilized", BIAS_BETA)):
+                    o = pna.attn_fwd_flash(q, kt, vt, causal=True, p_bf16=p_bf16, beta=bb,
+                                           out_f32=o_f32)
+                    o_s = torch.stack([o.view(b * h, n, d)[u] for u in BIAS_UNITS]).contiguous()
+                    dev = pna.attn_deviation(o_s, ref_t)
+                    row[kind] = {key: dev[key] for key in ("mean_signed", "mean_abs", "max_abs",
+                                                           "rms", "n_nonfinite")}
+                res[("o_fp32_" if o_f32 else "o_bf16_") + ("p_bf16" if p_bf16 else "p_fp32")] = row
         out[name] = res
     return out
 

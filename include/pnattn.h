@@ -99,6 +99,16 @@ typedef struct {
   float beta;          /* stabilized = 1: the factor beta > 1 (finite); the
                           page's own value is lost, so there is no default.
                           stabilized = 0: must be 0.                        */
+  int32_t o_f32;       /* 0: O in the V dtype (bf16 for ATTN_BF16, ATTN_INT8,
+                          ATTN_FP8).  1: O in fp32 whatever the inputs: the
+                          fp32 O = acc / l the kernels form, before any
+                          rounding to bf16 (so rounding it to bf16 gives the
+                          o_f32 = 0 output bit for bit).  This separates the
+                          rounding of O itself from the rounding upstream of
+                          it (the bf16 P of "Why Low-Precision Transformer
+                          Training Fails", Figures 5 and 7).  Both forward
+                          calls; the backward calls take bf16 O (o_f32 = 1 is
+                          ATTN_ERR_UNSUPPORTED there).                       */
 } attn_problem_t;
 
 /* FlashAttention forward ("Why Low-Precision Transformer Training Fails",
@@ -111,7 +121,8 @@ typedef struct {
  * O = acc / l at the end.  S is never stored.
  *   q, k   : [B,H,N,d] of dtype (int8 codes for ATTN_INT8, E4M3 bytes
  *            for ATTN_FP8)
- *   v, o   : [B,H,N,d] fp32 for ATTN_F32, bf16 otherwise
+ *   v      : [B,H,N,d] fp32 for ATTN_F32, bf16 otherwise
+ *   o      : [B,H,N,d], fp32 for ATTN_F32 or o_f32 = 1, bf16 otherwise
  *   q_scale, k_scale : [B,H,N] fp32, required for ATTN_INT8 and ATTN_FP8,
  *            else NULL
  *   lse    : optional [B,H,N] fp32 log-sum-exp of each score row (natural

@@ -32,6 +32,7 @@ class AttnProblem(ctypes.Structure):
         ("softmax_scale", ctypes.c_float),
         ("stabilized", ctypes.c_int32),
         ("beta", ctypes.c_float),
+        ("o_f32", ctypes.c_int32),
     ]
 
 
@@ -181,7 +182,7 @@ def _expect(t, name, shape, dtypes, like=None, required=True):
         raise ValueError(f"{name} is on {t.device}, q on {like.device}")
 
 
-def _check_attention(q, k, v, q_scale, k_scale, out, lse):
+def _check_attention(q, k, v, q_scale, k_scale, out, lse, out_f32=False):
     """Shapes and dtypes of the forward's tensors, all implied by q."""
     import torch
     if q.dim() != 4:
@@ -191,7 +192,7 @@ def _check_attention(q, k, v, q_scale, k_scale, out, lse):
     _expect(k, "k", q.shape, (q.dtype,), q)
     vtype = torch.float32 if q.dtype == torch.float32 else torch.bfloat16
     _expect(v, "v", q.shape, (vtype,), q)
-    _expect(out, "out", q.shape, (vtype,), q, required=False)
+    _expect(out, "out", q.shape, (torch.float32 if out_f32 else vtype,), q, required=False)
     _expect(lse, "lse", (b, h, n), (torch.float32,), q, required=False)
     scaled = q.dtype in (torch.int8, torch.uint8)
     for name, s in (("q_scale", q_scale), ("k_scale", k_scale)):
@@ -211,33 +212,37 @@ def _check_rows(x, codes, scales, code_dtype):
 
 
 def make_problem(q, *, causal: bool, p_bf16: bool = True, softmax_scale: float = 0.0,
-                 dtype: Optional[int] = None, beta: Optional[float] = None) -> AttnProblem:
-    """beta (> 1) selects the stabilised flash variant; None the standard one."""
+                 dtype: Optional[int] = None, beta: Optional[float] = None,
+                 out_f32: bool = False) -> AttnProblem:
+    """beta (> 1) selects the stabilised flash variant; None the standard one.
+    out_f32 asks for O in fp32 whatever the input dtype."""
     b, h, n, d = q.shape
     return AttnProblem(b, h, n, d, int(bool(causal)),
                        _dtype_code(q) if dtype is None else dtype, int(bool(p_bf16)),
                        float(softmax_scale), 0 if beta is None else 1,
-                       0.0 if beta is None else float(beta))
+                       0.0 if beta is None else float(beta), int(bool(out_f32)))
 
 
-def _out_like(q, v):
+def _out_like(q, v, out_f32=False):
     import torch
-    if q.dtype in (torch.int8, torch.uint8):
-        return torch.empty(q.shape[:-1] + (v.shape[-1],), dtype=v.dtype, device=v.device)
-    return torch.empty_like(v)
+    dt = torch.float32 if out_f32 else v.dtype
+    return torch.empty(q.shape[:-1] + (v.shape[-1],), dtype=dt, device=v.device)
 
 
 def attn_fwd_flash(q, k, v, *, causal: bool, p_bf16: bool = True, softmax_scale: float = 0.0,
-                   q_scale=None, k_scale=None, out=None, lse=None, beta=None, stream=None):
-    """FlashAttention forward; returns ``out`` ([B,H,N,d], dtype of v).
+                   q_scale=None, k_scale=None, out=None, lse=None, beta=None, out_f32=False,
+                   stream=None):
+    """FlashAttention forward; returns ``out`` ([B,H,N,d], dtype of v, or
+    fp32 with out_f32).
 
     beta (> 1, bf16 inputs only) runs the stabilised variant, whose
     normaliser is beta*r_m (r_m > 0) or 0 (r_m < 0) when the row max r_m
     occurs more than once."""
-    _check_attention(q, k, v, q_scale, k_scale, out, lse)
+    _check_attention(q, k, v, q_scale, k_scale, out, lse, out_f32)
     _contig(q, k, v, q_scale, k_scale, out, lse)
-    out = _out_like(q, v) if out is None else out
-    prob = make_problem(q, causal=causal, p_bf16=p_bf16, softmax_scale=softmax_scale, beta=beta)
+    out = _out_like(q, v, out_f32) if out is None else out
+    prob = make_problem(q, causal=causal, p_bf16=p_bf16, softmax_scale=softmax_scale, beta=beta,
+                        out_f32=out_f32)
     _check(load().attn_fwd_flash(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(q_scale),
                                  _ptr(k_scale), _ptr(out), _ptr(lse), _stream(stream)))
     return out
@@ -267,15 +272,17 @@ def attn_baseline_workspace_size(prob: AttnProblem) -> int:
 
 
 def attn_fwd_baseline(q, k, v, *, causal: bool, p_bf16: bool = True, softmax_scale: float = 0.0,
-                      q_scale=None, k_scale=None, workspace=None, out=None, stream=None):
+                      q_scale=None, k_scale=None, workspace=None, out=None, out_f32=False,
+                      stream=None):
     """Baseline attention (S and P in the workspace); returns (out, workspace)."""
     import torch
-    _check_attention(q, k, v, q_scale, k_scale, out, None)
+    _check_attention(q, k, v, q_scale, k_scale, out, None, out_f32)
     if workspace is not None and workspace.device != q.device:
         raise ValueError(f"workspace is on {workspace.device}, q on {q.device}")
     _contig(q, k, v, q_scale, k_scale, out, workspace)
-    out = _out_like(q, v) if out is None else out
-    prob = make_problem(q, causal=causal, p_bf16=p_bf16, softmax_scale=softmax_scale)
+    out = _out_like(q, v, out_f32) if out is None else out
+    prob = make_problem(q, causal=causal, p_bf16=p_bf16, softmax_scale=softmax_scale,
+                        out_f32=out_f32)
     need = attn_baseline_workspace_size(prob)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
@@ -397,7 +404,7 @@ def attn_bwd_delta(o, d_o, *, delta=None, stream=None):
     delta = (torch.empty((b, h, n), dtype=torch.float32, device=o.device)
              if delta is None else delta)
     code = ATTN_F32 if o.dtype == torch.float32 else ATTN_BF16
-    prob = AttnProblem(b, h, n, d, 0, code, 1, 0.0, 0, 0.0)
+    prob = AttnProblem(b, h, n, d, 0, code, 1, 0.0, 0, 0.0, 0)
     _check(load().attn_bwd_delta(ctypes.byref(prob), _ptr(o), _ptr(d_o), _ptr(delta),
                                  _stream(stream)))
     return delta

@@ -70,6 +70,8 @@ attn_status_t check_problem(const attn_problem_t* prob, const void* q, const voi
     return fail(ATTN_ERR_INVALID_ARG, "unknown dtype %d", prob->dtype);
   if (!std::isfinite(prob->softmax_scale))
     return fail(ATTN_ERR_INVALID_ARG, "softmax_scale is not finite");
+  if (prob->o_f32 != 0 && prob->o_f32 != 1)
+    return fail(ATTN_ERR_INVALID_ARG, "o_f32 must be 0 or 1 (got %d)", prob->o_f32);
   if (prob->stabilized != 0 && prob->stabilized != 1)
     return fail(ATTN_ERR_INVALID_ARG, "stabilized must be 0 or 1 (got %d)", prob->stabilized);
   if (prob->stabilized == 0 && prob->beta != 0.f)
@@ -104,6 +106,7 @@ attn_status_t check_problem(const attn_problem_t* prob, const void* q, const voi
   a->p_bf16 = prob->p_bf16;
   a->stabilized = prob->stabilized;
   a->beta = prob->beta;
+  a->o_f32 = prob->o_f32;
   a->scale = prob->softmax_scale > 0.f
                  ? prob->softmax_scale
                  : (float)(1.0 / std::sqrt((double)prob->head_dim));
@@ -152,7 +155,9 @@ attn_status_t attn_bwd_delta(const attn_problem_t* prob, const void* o, const vo
   if (rows == 0) return ok();
   if (o == nullptr || d_o == nullptr || delta == nullptr)
     return fail(ATTN_ERR_INVALID_ARG, "o, d_o and delta must be non-NULL");
-  const int out = prob->dtype == ATTN_F32 ? pn::kF32 : pn::kBF16;
+  if (prob->o_f32 != 0 && prob->o_f32 != 1)
+    return fail(ATTN_ERR_INVALID_ARG, "o_f32 must be 0 or 1 (got %d)", prob->o_f32);
+  const int out = (prob->dtype == ATTN_F32 || prob->o_f32) ? pn::kF32 : pn::kBF16;
   return from_hip(pn::launch_delta(o, d_o, out, (int)prob->head_dim, rows, delta,
                                    (hipStream_t)stream),
                   "attn_bwd_delta launch");
@@ -181,6 +186,8 @@ attn_status_t attn_bwd_flash(const attn_problem_t* prob, const void* q, const vo
     return fail(ATTN_ERR_UNSUPPORTED, "attn_bwd_flash is built for ATTN_BF16 only");
   if (prob->stabilized != 0)
     return fail(ATTN_ERR_UNSUPPORTED, "attn_bwd_flash is the standard variant's backward");
+  if (prob->o_f32 != 0)
+    return fail(ATTN_ERR_UNSUPPORTED, "attn_bwd_flash takes the bf16 forward output");
   if (empty) return ok();
   if (d_o == nullptr || lse == nullptr || dq == nullptr || dk == nullptr || dv == nullptr ||
       workspace == nullptr)

@@ -198,7 +198,7 @@ __global__ __launch_bounds__(kThreads) void softmax_kernel(const void* sp, void*
 // O^T = V^T P^T: V^T through the transposing LDS read, P^T straight from its
 // row-major tile.
 // ---------------------------------------------------------------------------
-template <int D, typename PT, typename VT>
+template <int D, typename PT, typename VT, typename OT>
 __global__ __launch_bounds__(kThreads) void pv_kernel(const void* pp, const void* vp, void* op,
                                                      int N) {
   constexpr bool BF16MMA = sizeof(PT) == 2 && sizeof(VT) == 2;
@@ -280,7 +280,7 @@ __global__ __launch_bounds__(kThreads) void pv_kernel(const void* pp, const void
   }
   const int q = q0 + 32 * wave + n;
   if (q < N) {
-    VT* dst = (VT*)op + (bh * N + q) * (int64_t)D;
+    OT* dst = (OT*)op + (bh * N + q) * (int64_t)D;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -288,7 +288,7 @@ __global__ __launch_bounds__(kThreads) void pv_kernel(const void* pp, const void
         const int d0 = 32 * dt + 8 * b4 + 4 * g;
         const float x0 = oacc[dt][4 * b4], x1 = oacc[dt][4 * b4 + 1];
         const float x2 = oacc[dt][4 * b4 + 2], x3 = oacc[dt][4 * b4 + 3];
-        if constexpr (sizeof(VT) == 2) {
+        if constexpr (sizeof(OT) == 2) {
           uint2 w;
           w.x = (uint32_t)f32_to_bf16(x0) | ((uint32_t)f32_to_bf16(x1) << 16);
           w.y = (uint32_t)f32_to_bf16(x2) | ((uint32_t)f32_to_bf16(x3) << 16);
@@ -321,14 +321,19 @@ hipError_t launch_pv(const AttnArgs& a, const void* p, hipStream_t st) {
   const int N = (int)a.seq_len;
   dim3 grid((N + 127) / 128, (unsigned)(a.batch * a.heads));
   const bool vf32 = a.dtype == kF32;
-  if (a.p_bf16 && !vf32)
-    hipLaunchKernelGGL((pv_kernel<D, uint16_t, uint16_t>), grid, dim3(kThreads), 0, st, p, a.v, a.o, N);
-  else if (a.p_bf16 && vf32)
-    hipLaunchKernelGGL((pv_kernel<D, uint16_t, float>), grid, dim3(kThreads), 0, st, p, a.v, a.o, N);
+  const bool of32 = vf32 || a.o_f32;  // fp32 V always gives fp32 O
+  if (a.p_bf16 && !vf32 && !of32)
+    hipLaunchKernelGGL((pv_kernel<D, uint16_t, uint16_t, uint16_t>), grid, dim3(kThreads), 0, st, p, a.v, a.o, N);
+  else if (a.p_bf16 && !vf32)
+    hipLaunchKernelGGL((pv_kernel<D, uint16_t, uint16_t, float>), grid, dim3(kThreads), 0, st, p, a.v, a.o, N);
+  else if (a.p_bf16)
+    hipLaunchKernelGGL((pv_kernel<D, uint16_t, float, float>), grid, dim3(kThreads), 0, st, p, a.v, a.o, N);
+  else if (!vf32 && !of32)
+    hipLaunchKernelGGL((pv_kernel<D, float, uint16_t, uint16_t>), grid, dim3(kThreads), 0, st, p, a.v, a.o, N);
   else if (!vf32)
-    hipLaunchKernelGGL((pv_kernel<D, float, uint16_t>), grid, dim3(kThreads), 0, st, p, a.v, a.o, N);
+    hipLaunchKernelGGL((pv_kernel<D, float, uint16_t, float>), grid, dim3(kThreads), 0, st, p, a.v, a.o, N);
   else
-    hipLaunchKernelGGL((pv_kernel<D, float, float>), grid, dim3(kThreads), 0, st, p, a.v, a.o, N);
+    hipLaunchKernelGGL((pv_kernel<D, float, float, float>), grid, dim3(kThreads), 0, st, p, a.v, a.o, N);
   return hipGetLastError();
 }
 

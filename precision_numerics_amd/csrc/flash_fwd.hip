@@ -122,6 +122,7 @@ struct FlashParams {
   int n;             // sequence length
   float scale_log2;  // softmax scale * log2(e)
   int p_round;       // fp32 P*V engines: round P to bf16 values first
+  int o_f32;         // store O in fp32 (else in the V dtype)
   float beta;        // stabilised variant: normaliser factor for a repeated positive max
   int64_t bh_count;  // batch * heads
   int q_tiles;       // query tiles per (batch, head)
@@ -844,7 +845,8 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
     const float l_tot = pair32_sum(l_run);
     const float inv = 1.f / l_tot;
     if (row < N) {
-      VT* dst = (VT*)p.o + (int64_t)b * N * D + (int64_t)row * D;
+      const int64_t base = (int64_t)b * N * D + (int64_t)row * D;
+      const bool f32out = sizeof(VT) == 4 || p.o_f32 != 0;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -852,13 +854,13 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
           const int d0 = 32 * dt + 8 * b4 + 4 * g;
           const float x0 = oacc[dt][4 * b4 + 0] * inv, x1 = oacc[dt][4 * b4 + 1] * inv;
           const float x2 = oacc[dt][4 * b4 + 2] * inv, x3 = oacc[dt][4 * b4 + 3] * inv;
-          if constexpr (sizeof(VT) == 2) {
+          if (f32out) {
+            *(float4*)((float*)p.o + base + d0) = make_float4(x0, x1, x2, x3);
+          } else {
             uint2 w;
             w.x = (uint32_t)f32_to_bf16(x0) | ((uint32_t)f32_to_bf16(x1) << 16);
             w.y = (uint32_t)f32_to_bf16(x2) | ((uint32_t)f32_to_bf16(x3) << 16);
-            *(uint2*)(dst + d0) = w;
-          } else {
-            *(float4*)(dst + d0) = make_float4(x0, x1, x2, x3);
+            *(uint2*)((uint16_t*)p.o + base + d0) = w;
           }
         }
       if (p.lse != nullptr && g == 0) p.lse[(int64_t)b * N + row] = (m_run + __log2f(l_tot)) * kLn2;
@@ -1080,6 +1082,7 @@ hipError_t launch_flash(const AttnArgs& a, hipStream_t stream) {
   fp.n = (int)a.seq_len;
   fp.scale_log2 = (float)((double)a.scale * 1.4426950408889634);
   fp.p_round = (a.dtype == kF32) ? a.p_bf16 : 0;
+  fp.o_f32 = a.o_f32;
   fp.beta = a.beta;
   const int64_t bh = a.batch * a.heads;
   const int ntiles = (int)((a.seq_len + kBR - 1) / kBR);

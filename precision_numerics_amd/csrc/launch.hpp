@@ -26,6 +26,7 @@ struct AttnArgs {
   float scale = 0.f;  // resolved softmax scale (> 0)
   int stabilized = 0; // flash only: the repeated-max normaliser variant
   float beta = 0.f;   // its factor (> 1) for a repeated positive max
+  int o_f32 = 0;      // O in fp32 (else in the V dtype)
 };
 
 // Flash forward; returns the launch status.

@@ -65,6 +65,7 @@ FAKE = 0x1000  # never dereferenced: every case below fails validation first
     (dict(stabilized=0, beta=2.0), B.ATTN_ERR_INVALID_ARG),  # beta without the variant
     (dict(stabilized=1, beta=2.0, dtype=B.ATTN_F32), B.ATTN_ERR_UNSUPPORTED),
     (dict(dtype=B.ATTN_INT8), B.ATTN_ERR_INVALID_ARG),       # scales missing
+    (dict(o_f32=2), B.ATTN_ERR_INVALID_ARG),
 ])
 def test_flash_validation(clib, kw, status):
     p = _prob(**kw)
@@ -230,3 +231,11 @@ def test_backward_validation(clib):
     assert BW(ctypes.byref(ps), *args, 1 << 20, None) == 2
     empty = _prob(seq_len=0)
     assert BW(ctypes.byref(empty), *([None] * 10), 0, None) == 0
+
+
+def test_backward_takes_bf16_output(clib):
+    p = _prob(o_f32=1)
+    rc = clib.attn_bwd_flash(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                             FAKE, FAKE, 1 << 20, None)
+    assert rc == B.ATTN_ERR_UNSUPPORTED
+    assert "bf16" in clib.attn_last_error().decode()

@@ -184,3 +184,11 @@ def test_well_formed_calls_reach_the_device_check(call):
     }
     with pytest.raises(ValueError, match="CUDA"):
         calls[call]()
+
+
+def test_out_f32_needs_an_fp32_buffer():
+    q, k, v = qkv()
+    with pytest.raises(TypeError, match="out has dtype"):
+        pna.attn_fwd_flash(q, k, v, causal=True, out_f32=True, out=t((B, H, N, D), bf16))
+    with pytest.raises(ValueError, match="CUDA"):
+        pna.attn_fwd_flash(q, k, v, causal=True, out_f32=True, out=t((B, H, N, D), f32))
