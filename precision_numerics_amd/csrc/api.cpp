@@ -236,6 +236,8 @@ attn_status_t attn_fwd_flash_debug_s(const attn_problem_t* prob, const void* q, 
   if (st != ATTN_OK) return st;
   if (prob->dtype != ATTN_INT8)
     return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd_flash_debug_s is for ATTN_INT8 only");
+  if (prob->o_f32 != 0)
+    return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd_flash_debug_s writes a bf16 output");
   if (empty) return ok();
   if (s_out == nullptr) return fail(ATTN_ERR_INVALID_ARG, "s_out is NULL");
   a.s_dbg = s_out;

@@ -103,10 +103,12 @@ template <int D, int QK, int PV> struct Tile {
   static constexpr int kSegVPerWave = (kSegV + kIssuers - 1) / kIssuers;
   static constexpr int kSegPerWave = kSegKPerWave > kSegVPerWave ? kSegKPerWave : kSegVPerWave;
   static constexpr int kBytesSk = kScaledQK<QK> ? kBC * 4 : 0;
-  // [K buf0][K buf1][V buf0][V buf1][sk buf0][sk buf1]
+  // [K buf0][K buf1][V buf0][V buf1][sk buf0][sk buf1][sk buf2].  The key
+  // scales of block j are read in the softmax half-step X_j, which group 1
+  // runs while group 0 already loads block j + 2: they take three buffers.
   static constexpr int kOffV = 2 * kBytesK;
   static constexpr int kOffSk = kOffV + 2 * kBytesV;
-  static constexpr int kLds = kOffSk + 2 * kBytesSk;
+  static constexpr int kLds = kOffSk + 3 * kBytesSk;
   static_assert(kBytesK % 1024 == 0 && kBytesV % 1024 == 0, "tiles must be whole segments");
 };
 
@@ -122,7 +124,6 @@ struct FlashParams {
   int n;             // sequence length
   float scale_log2;  // softmax scale * log2(e)
   int p_round;       // fp32 P*V engines: round P to bf16 values first
-  int o_f32;         // store O in fp32 (else in the V dtype)
   float beta;        // stabilised variant: normaliser factor for a repeated positive max
   int64_t bh_count;  // batch * heads
   int q_tiles;       // query tiles per (batch, head)
@@ -270,11 +271,23 @@ __device__ __forceinline__ void s_schedule() {
 }
 
 
-// Issue this wave's share (w = 0..3 inside the issuing group) of the loads
-// that fill K tile buffer `buf` with key rows kb.. (and, for int8, the key
-// scales).  Asynchronous.
+// The key scales of rows kb.. into key-scale buffer skbuf (one wave).
 template <int D, int QK, int PV>
-__device__ __forceinline__ void issue_k(char* smem, int w, int lane, int kb, int buf,
+__device__ __forceinline__ void issue_sk(char* smem, int lane, int kb, int skbuf,
+                                         const void* sbase, int n) {
+  using TL = Tile<D, QK, PV>;
+  const i32x4 rsS = buffer_rsrc(sbase, (uint32_t)n * 4);
+#pragma unroll
+  for (int h = 0; h < TL::kBC / 64; ++h)
+    lds_load4(rsS, (uint32_t)lane * 4, (uint32_t)(kb + 64 * h) * 4,
+              lds_address(smem) + TL::kOffSk + skbuf * TL::kBytesSk + 256 * h);
+}
+
+// Issue this wave's share (w = 0..3 inside the issuing group) of the loads
+// that fill K tile buffer `buf` with key rows kb.. (and, for 8-bit Q/K, the
+// key scales into key-scale buffer skbuf).  Asynchronous.
+template <int D, int QK, int PV>
+__device__ __forceinline__ void issue_k(char* smem, int w, int lane, int kb, int buf, int skbuf,
                                         const void* kbase, const void* sbase, int n,
                                         const uint32_t* voffK) {
   using TL = Tile<D, QK, PV>;
@@ -287,13 +300,7 @@ __device__ __forceinline__ void issue_k(char* smem, int w, int lane, int kb, int
       lds_load16<i * TL::kIssuers * 1024>(rsK, voffK[i], soff, base);
   });
   if constexpr (kScaledQK<QK>) {
-    if (w == 0) {
-      const i32x4 rsS = buffer_rsrc(sbase, (uint32_t)n * 4);
-#pragma unroll
-      for (int h = 0; h < TL::kBC / 64; ++h)
-        lds_load4(rsS, (uint32_t)lane * 4, (uint32_t)(kb + 64 * h) * 4,
-                  lds_address(smem) + TL::kOffSk + buf * TL::kBytesSk + 256 * h);
-    }
+    if (w == 0) issue_sk<D, QK, PV>(smem, lane, kb, skbuf, sbase, n);
   }
 }
 
@@ -335,7 +342,7 @@ __device__ __forceinline__ void block_barrier() {
 // issue and wait points).  The kernel is persistent: a workgroup walks a
 // list of query tiles, and one tile's last slots overlap the next one's
 // first.
-template <int D, int QK, int PV, bool CAUSAL, bool DEBUG_S, bool STAB>
+template <int D, int QK, int PV, bool CAUSAL, bool DEBUG_S, bool STAB, bool OF32>
 __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
   using QT = typename QKTraits<QK>::T;
   using VT = typename VTraits<PV>::T;
@@ -358,6 +365,7 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
   // ---- the tile this workgroup works on (its identity changes at the
   // switch to the next tile), and the next one
   int round = 0;
+  int jg0 = 0;  // global number of the current tile's first key block
   TileId cur = tile_of<CAUSAL, BC>(p, 0);
   TileId nxt = tile_of<CAUSAL, BC>(p, 1);
   if (!cur.valid) return;  // never: the grid has at most `tiles` workgroups
@@ -379,14 +387,15 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
 
   // The first K tile streams in while this lane's Q row loads.
   if (group == 0)
-    issue_k<D, QK, PV>(smem, wg, lane, 0, 0, head_ptr(p.k, bh, sizeof(QT)),
+    issue_k<D, QK, PV>(smem, wg, lane, 0, 0, 0, head_ptr(p.k, bh, sizeof(QT)),
                        kScaledQK<QK> ? (const void*)(p.k_scale + (int64_t)bh * N) : nullptr, N, voff);
 
   // ---- this lane's query row as the B operand of S^T = K Q^T (registers)
   constexpr int QST = (QK == QK_BF16) ? D / 16 : (kScaledQK<QK> ? D / 32 : D / 2);
   i32x4 qv[QK == QK_F32 ? 1 : QST];
   float qf[QK == QK_F32 ? QST : 1];
-  float sq_log2 = 0.f;
+  float sq_log2 = 0.f;  // this tile's row scale times scale * log2(e) (8-bit Q/K)
+  float sq_pend = 0.f;  // the same for the tile whose Q rows were loaded last
   // load the Q row of query `row` of head `b` (zeros past the sequence end)
   auto load_q = [&](int b, int row) __attribute__((always_inline)) {
     const bool ok = row < N;
@@ -401,10 +410,11 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
         const QT* src = Qg + (int64_t)row * D + 2 * EPC * t + EPC * g;
         qv[t] = ok ? *(const i32x4*)src : i32x4{0, 0, 0, 0};
       }
-      if constexpr (kScaledQK<QK>) sq_log2 = ok ? p.q_scale[(int64_t)b * N + row] * p.scale_log2 : 0.f;
+      if constexpr (kScaledQK<QK>) sq_pend = ok ? p.q_scale[(int64_t)b * N + row] * p.scale_log2 : 0.f;
     }
   };
   load_q(bh, qrow);
+  sq_log2 = sq_pend;
 
   // One wait for the Q row and the first K tile, with a wait the compiler
   // sees: otherwise its wait-count pass, unsure the Q loads finished before
@@ -452,16 +462,19 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
   struct Prefetch {
     const void* base;
     const void* sbase;
-    int kb, buf;
+    int kb, buf, skbuf;
     bool on;
   };
-  // this wave's K segment q of a request
+  // this wave's K segment q of a request (with the first, the key scales)
   auto issue_one = [&](auto qc, const Prefetch& rq) __attribute__((always_inline)) {
     constexpr int q = decltype(qc)::value;
     if (rq.on && (TL::kSegK % TL::kIssuers == 0 || wg + q * TL::kIssuers < TL::kSegK))
       lds_load16<q * TL::kIssuers * 1024>(
           buffer_rsrc(rq.base, (uint32_t)N * TL::kRowK), voff[q], (uint32_t)rq.kb * TL::kRowK,
           lds_address(smem) + rq.buf * TL::kBytesK + wg * 1024);
+    if constexpr (q == 0 && kScaledQK<QK>) {
+      if (rq.on && wg == 0) issue_sk<D, QK, PV>(smem, lane, rq.kb, rq.skbuf, rq.sbase, N);
+    }
   };
 
   // The fp8 engine runs out of registers when the source offsets of this
@@ -472,6 +485,11 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
   // since the recomputation costs vector instructions in the matrix
   // half-step.
   constexpr bool kFreshVoff = QK == QK_F8;
+  // The fenced matrix half-step (products and LDS reads only) serves bf16 P
+  // with bf16, int8 or fp8 Q/K; 8-bit scores get their key scales in the
+  // softmax half-step.
+  constexpr bool kFenced = PV == PV_BF16 && (QK == QK_BF16 || kScaledQK<QK>);
+  constexpr bool kScaleInX = kFenced && kScaledQK<QK>;
   auto fresh_voff = [&](uint32_t (&dst)[TL::kSegPerWave]) __attribute__((always_inline)) {
     int l = lane;
     asm volatile("" : "+v"(l));
@@ -498,7 +516,7 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
         if (rq.on) issue_v<D, QK, PV>(smem, wg, rq.kb, rq.buf, rq.base, N, vo);
       }
     }
-    if constexpr (PV == PV_BF16 && QK == QK_BF16) {
+    if constexpr (kFenced) {
       // The whole half-step in program order, fenced so that the scheduler
       // keeps it: product i is followed by the LDS reads of product
       // i + kAhead, so every operand is requested kAhead products (about
@@ -536,9 +554,17 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
         if (i < NPV) {
           oacc[i % DT] = mfma_bf16(join_bf16x8(vlo[i], vhi[i]), pb[i / DT], oacc[i % DT]);
         } else {
+          // 8-bit Q/K: raw int32 (or fp32 fp8) products; the softmax
+          // half-step applies the key scales
           const int t = i - NPV;
-          s[t / QST] = mfma_bf16(__builtin_bit_cast(bf16x8, kf[t]),
-                                 __builtin_bit_cast(bf16x8, qv[t % QST]), s[t / QST]);
+          if constexpr (QK == QK_BF16)
+            s[t / QST] = mfma_bf16(__builtin_bit_cast(bf16x8, kf[t]),
+                                   __builtin_bit_cast(bf16x8, qv[t % QST]), s[t / QST]);
+          else if constexpr (QK == QK_I8)
+            s[t / QST] = __builtin_bit_cast(
+                f32x16, mfma_i8(kf[t], qv[t % QST], __builtin_bit_cast(i32x16, s[t / QST])));
+          else
+            s[t / QST] = mfma_fp8x2(kf[t], qv[t % QST], s[t / QST]);
         }
       };
       // The wave sharing this SIMD runs its softmax meanwhile; a dense VALU
@@ -561,6 +587,33 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
       }
       __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_setprio(0);
+      if constexpr (DEBUG_S && DO_S) {
+        if (qvalid) {
+          int32_t* dst = p.s_dbg + ((int64_t)bh * N + qrow) * (int64_t)N;
+#pragma unroll
+          for (int ks = 0; ks < NKS; ++ks) {
+            // whole-vector cast: a bit_cast of one element of a vector
+            // register is lowered as a read of element 0
+            const i32x16 si = __builtin_bit_cast(i32x16, s[ks]);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int key = jl * BC + 32 * ks + elem_of_reg(r, g);
+              if (key < N) dst[key] = si[r];
+            }
+          }
+        }
+      }
+      if constexpr (DO_S && QK == QK_I8) {
+        // exact int32 -> fp32 (|products| < 2^24) while the other wave of the
+        // SIMD still runs its softmax; the key scales follow in this
+        // wave's softmax half-step
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+          const i32x16 si = __builtin_bit_cast(i32x16, s[ks]);  // whole-vector cast
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s[ks][r] = (float)si[r];
+        }
+      }
       if constexpr (DO_S) {
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) pin(s[ks]);  // raw q.k; scaled inside exp2
@@ -578,11 +631,11 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
     } else {
       if constexpr (ISSUE == 1) {
         if constexpr (!kFreshVoff) {
-          if (rq.on) issue_k<D, QK, PV>(smem, wg, lane, rq.kb, rq.buf, rq.base, rq.sbase, N, voff);
+          if (rq.on) issue_k<D, QK, PV>(smem, wg, lane, rq.kb, rq.buf, rq.skbuf, rq.base, rq.sbase, N, voff);
         } else {
           uint32_t vo[TL::kSegPerWave];
           fresh_voff(vo);
-          if (rq.on) issue_k<D, QK, PV>(smem, wg, lane, rq.kb, rq.buf, rq.base, rq.sbase, N, vo);
+          if (rq.on) issue_k<D, QK, PV>(smem, wg, lane, rq.kb, rq.buf, rq.skbuf, rq.base, rq.sbase, N, vo);
         }
       }
       if constexpr (DO_PV) {
@@ -654,7 +707,7 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) s[ks][r] = acc[ks][r];  // raw q.k; scaled inside exp2
         } else if constexpr (QK == QK_I8) {
-          const float* skt = (const float*)(smem + TL::kOffSk + (jg & 1) * TL::kBytesSk);
+          const float* skt = (const float*)(smem + TL::kOffSk + (jg % 3) * TL::kBytesSk);
 #pragma unroll
           for (int ks = 0; ks < NKS; ++ks) {
             const char* krow = kt + ks * 32 * TL::kStrK + k_lane + 16 * g;
@@ -680,7 +733,7 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
         } else if constexpr (QK == QK_F8) {
           // E4M3 codes in the int8 layout: two fp8 products per 32-byte
           // chunk of the row, then the per-row scales as for int8
-          const float* skt = (const float*)(smem + TL::kOffSk + (jg & 1) * TL::kBytesSk);
+          const float* skt = (const float*)(smem + TL::kOffSk + (jg % 3) * TL::kBytesSk);
 #pragma unroll
           for (int ks = 0; ks < NKS; ++ks) {
             const char* krow = kt + ks * 32 * TL::kStrK + k_lane + 16 * g;
@@ -710,6 +763,24 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
   // ================= X_j: online softmax of block j
   auto half_x = [&](const int j) __attribute__((always_inline)) {
     const int kb = j * BC;
+    if constexpr (kScaleInX) {
+      // t = code product * key scale; the row's scale enters with the exp2
+      // argument (it is positive, so the row max is taken on t).  The
+      // products are fp32 here (int8: converted in the matrix step).
+      const float* skt = (const float*)(smem + TL::kOffSk + ((jg0 + j) % 3) * TL::kBytesSk);
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const f32x4 a0 = *(const f32x4*)(skt + 32 * ks + 8 * g);
+        const f32x4 a1 = *(const f32x4*)(skt + 32 * ks + 8 * g + 4);
+        const f32x4 b0 = *(const f32x4*)(skt + 32 * ks + 16 + 8 * g);
+        const f32x4 b1 = *(const f32x4*)(skt + 32 * ks + 16 + 8 * g + 4);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float sk = r < 4 ? a0[r] : r < 8 ? a1[r - 4] : r < 12 ? b0[r - 8] : b1[r - 12];
+          s[ks][r] *= sk;  // products already fp32 (int8: converted in the matrix step)
+        }
+      }
+    }
     // causal diagonal and ragged tail: invisible keys score -inf.  The test
     // is per 32-key subtile first (uniform across the wave): subtiles wholly
     // visible are left alone, wholly invisible ones are set to -inf, and
@@ -749,10 +820,11 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
         }
       }
     }
-    // bf16/fp32 Q,K: s holds raw dot products; the max is taken on them
-    // (the scale is positive) and P = exp2(fma(s, c, -m)) with
-    // m = c * max: one fma and one v_exp per score.  int8: s is already
-    // in log2 units (per-key scales), P = exp2(s - m).
+    // bf16/fp32 Q,K: s holds raw dot products; int8/fp8 Q,K with bf16 P:
+    // code products times key scales.  The max is taken on them (the row
+    // factor c is positive) and P = exp2(fma(s, c, -m)) with m = c * max:
+    // one fma and one v_exp per score.  int8/fp8 with fp32 P: s is already
+    // in log2 units, P = exp2(s - m).
     float flat[NKS * 16];
 #pragma unroll
     for (int i = 0; i < NKS * 16; ++i) flat[i] = s[i / 16][i % 16];
@@ -761,7 +833,11 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
     const float mraw_new = fmaxf(mraw_run, mx);
     // normaliser m of this block's probabilities P = exp2(s*c - m), in log2
     // units (int8: s is already scaled)
-    float m_use = kScaledQK<QK> ? mraw_new : mraw_new * p.scale_log2;
+    // score factor: scale * log2(e) (bf16/fp32 Q, K), the row's
+    // q_scale * scale * log2(e) (8-bit Q/K scaled here), none (8-bit Q/K
+    // scaled in the matrix half-step)
+    const float row_c = kScaleInX ? sq_log2 : p.scale_log2;
+    float m_use = (kScaledQK<QK> && !kScaleInX) ? mraw_new : mraw_new * row_c;
     if constexpr (STAB) {
       // Stabilised variant ("Why Low-Precision Transformer Training Fails",
       // Figure 7 and Algorithm 1): when the row maximum r_m occurs more than
@@ -800,10 +876,10 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
     for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        if constexpr (kScaledQK<QK>)
+        if constexpr (kScaledQK<QK> && !kScaleInX)
           s[ks][r] = exp2_approx(s[ks][r] - m_use);
         else
-          s[ks][r] = exp2_approx(__builtin_fmaf(s[ks][r], p.scale_log2, -m_use));
+          s[ks][r] = exp2_approx(__builtin_fmaf(s[ks][r], row_c, -m_use));
         rsum[r & 3] += s[ks][r];
       }
     l_run = l_run * alpha + ((rsum[0] + rsum[1]) + (rsum[2] + rsum[3]));
@@ -846,7 +922,9 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
     const float inv = 1.f / l_tot;
     if (row < N) {
       const int64_t base = (int64_t)b * N * D + (int64_t)row * D;
-      const bool f32out = sizeof(VT) == 4 || p.o_f32 != 0;
+      // O in fp32 (fp32 V, or asked for: a separate instance, so that the
+      // bf16-output kernels carry no trace of it)
+      constexpr bool f32out = sizeof(VT) == 4 || OF32;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -854,7 +932,7 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
           const int d0 = 32 * dt + 8 * b4 + 4 * g;
           const float x0 = oacc[dt][4 * b4 + 0] * inv, x1 = oacc[dt][4 * b4 + 1] * inv;
           const float x2 = oacc[dt][4 * b4 + 2] * inv, x3 = oacc[dt][4 * b4 + 3] * inv;
-          if (f32out) {
+          if constexpr (f32out) {
             *(float4*)((float*)p.o + base + d0) = make_float4(x0, x1, x2, x3);
           } else {
             uint2 w;
@@ -900,8 +978,7 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
   constexpr IntC<0> kIssueNone{};
   constexpr IntC<1> kIssueK{};
   constexpr IntC<2> kIssueV{};
-  const Prefetch kNone{nullptr, nullptr, 0, 0, false};
-  int jg0 = 0;             // global number of the current tile's first block
+  const Prefetch kNone{nullptr, nullptr, 0, 0, 0, false};
   bool pending = false;    // a finished tile's O waits in the registers
   int pend_bh = 0;
   int pend_row = 0;
@@ -911,11 +988,12 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
     const int b = same ? cur.bh : nxt.bh;
     return Prefetch{head_ptr(p.k, b, sizeof(QT)),
                     kScaledQK<QK> ? (const void*)(p.k_scale + (int64_t)b * N) : nullptr,
-                    same ? (j + 1) * BC : 0, (jg0 + j + 1) & 1, same || nxt.valid};
+                    same ? (j + 1) * BC : 0, (jg0 + j + 1) & 1, (jg0 + j + 1) % 3,
+                    same || nxt.valid};
   };
   // the V block of local block j of the current tile
   auto this_v = [&](int j) __attribute__((always_inline)) {
-    return Prefetch{head_ptr(p.v, cur.bh, sizeof(VT)), nullptr, j * BC, (jg0 + j) & 1, true};
+    return Prefetch{head_ptr(p.v, cur.bh, sizeof(VT)), nullptr, j * BC, (jg0 + j) & 1, 0, true};
   };
   // start of X_j: the finished tile's output, the next tile's Q rows
   auto x_prologue = [&](int j) __attribute__((always_inline)) {
@@ -938,6 +1016,7 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
     q0w = cur.q0 + wave * 32;
     qrow = q0w + n;
     qvalid = qrow < N;
+    sq_log2 = sq_pend;
   };
 
   if (group == 0) {
@@ -1007,43 +1086,48 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
   }
 }
 
-template <int D, int QK, int PV, bool CAUSAL, bool DEBUG_S, bool STAB>
-hipError_t launch_t(const FlashParams& fp, int64_t bh, int ntiles, hipStream_t st) {
-  (void)bh;
-  (void)ntiles;
-  hipLaunchKernelGGL((flash_fwd_kernel<D, QK, PV, CAUSAL, DEBUG_S, STAB>), dim3(fp.grid),
+template <int D, int QK, int PV, bool CAUSAL, bool DEBUG_S, bool STAB, bool OF32>
+hipError_t launch_t(const FlashParams& fp, hipStream_t st) {
+  hipLaunchKernelGGL((flash_fwd_kernel<D, QK, PV, CAUSAL, DEBUG_S, STAB, OF32>), dim3(fp.grid),
                      dim3(kThreads), 0, st, fp);
   return hipGetLastError();
 }
 
-template <int D, int QK, int PV, bool DEBUG_S, bool STAB = false>
-hipError_t launch_c(const FlashParams& fp, bool causal, int64_t bh, int nt, hipStream_t st) {
-  return causal ? launch_t<D, QK, PV, true, DEBUG_S, STAB>(fp, bh, nt, st)
-                : launch_t<D, QK, PV, false, DEBUG_S, STAB>(fp, bh, nt, st);
+template <int D, int QK, int PV, bool DEBUG_S, bool STAB, bool OF32>
+hipError_t launch_c(const FlashParams& fp, bool causal, hipStream_t st) {
+  return causal ? launch_t<D, QK, PV, true, DEBUG_S, STAB, OF32>(fp, st)
+                : launch_t<D, QK, PV, false, DEBUG_S, STAB, OF32>(fp, st);
+}
+
+// bf16 or fp32 output
+template <int D, int QK, int PV, bool STAB = false>
+hipError_t launch_o(const FlashParams& fp, bool causal, bool of32, hipStream_t st) {
+  return of32 ? launch_c<D, QK, PV, false, STAB, true>(fp, causal, st)
+              : launch_c<D, QK, PV, false, STAB, false>(fp, causal, st);
 }
 
 template <int D>
-hipError_t launch_d(const AttnArgs& a, const FlashParams& fp, int64_t bh, int nt,
-                    hipStream_t st) {
+hipError_t launch_d(const AttnArgs& a, const FlashParams& fp, hipStream_t st) {
   const bool c = a.causal != 0;
+  const bool o = a.o_f32 != 0;
   switch (a.dtype) {
     case kF32:
-      return launch_c<D, QK_F32, PV_F32_VF32, false>(fp, c, bh, nt, st);
+      return launch_c<D, QK_F32, PV_F32_VF32, false, false, false>(fp, c, st);
     case kBF16:
       if (a.stabilized)
-        return a.p_bf16 ? launch_c<D, QK_BF16, PV_BF16, false, true>(fp, c, bh, nt, st)
-                        : launch_c<D, QK_BF16, PV_F32_VBF16, false, true>(fp, c, bh, nt, st);
-      return a.p_bf16 ? launch_c<D, QK_BF16, PV_BF16, false>(fp, c, bh, nt, st)
-                      : launch_c<D, QK_BF16, PV_F32_VBF16, false>(fp, c, bh, nt, st);
+        return a.p_bf16 ? launch_o<D, QK_BF16, PV_BF16, true>(fp, c, o, st)
+                        : launch_o<D, QK_BF16, PV_F32_VBF16, true>(fp, c, o, st);
+      return a.p_bf16 ? launch_o<D, QK_BF16, PV_BF16>(fp, c, o, st)
+                      : launch_o<D, QK_BF16, PV_F32_VBF16>(fp, c, o, st);
     case kINT8:
       if (a.s_dbg != nullptr)
-        return a.p_bf16 ? launch_c<D, QK_I8, PV_BF16, true>(fp, c, bh, nt, st)
-                        : launch_c<D, QK_I8, PV_F32_VBF16, true>(fp, c, bh, nt, st);
-      return a.p_bf16 ? launch_c<D, QK_I8, PV_BF16, false>(fp, c, bh, nt, st)
-                      : launch_c<D, QK_I8, PV_F32_VBF16, false>(fp, c, bh, nt, st);
+        return a.p_bf16 ? launch_c<D, QK_I8, PV_BF16, true, false, false>(fp, c, st)
+                        : launch_c<D, QK_I8, PV_F32_VBF16, true, false, false>(fp, c, st);
+      return a.p_bf16 ? launch_o<D, QK_I8, PV_BF16>(fp, c, o, st)
+                      : launch_o<D, QK_I8, PV_F32_VBF16>(fp, c, o, st);
     case kFP8:
-      return a.p_bf16 ? launch_c<D, QK_F8, PV_BF16, false>(fp, c, bh, nt, st)
-                      : launch_c<D, QK_F8, PV_F32_VBF16, false>(fp, c, bh, nt, st);
+      return a.p_bf16 ? launch_o<D, QK_F8, PV_BF16>(fp, c, o, st)
+                      : launch_o<D, QK_F8, PV_F32_VBF16>(fp, c, o, st);
   }
   return hipErrorInvalidValue;
 }
@@ -1082,7 +1166,6 @@ hipError_t launch_flash(const AttnArgs& a, hipStream_t stream) {
   fp.n = (int)a.seq_len;
   fp.scale_log2 = (float)((double)a.scale * 1.4426950408889634);
   fp.p_round = (a.dtype == kF32) ? a.p_bf16 : 0;
-  fp.o_f32 = a.o_f32;
   fp.beta = a.beta;
   const int64_t bh = a.batch * a.heads;
   const int ntiles = (int)((a.seq_len + kBR - 1) / kBR);
@@ -1101,8 +1184,8 @@ hipError_t launch_flash(const AttnArgs& a, hipStream_t stream) {
   // workgroup a balanced share (e.g. 1.5 rounds of 2/4/6/8-block tiles: at most
   // 8 blocks per workgroup, against 10 in head groups).
   fp.grp4 = (bh % 32 == 0 && fp.grid % 8 == 0 && fp.tiles >= 2 * (int64_t)fp.grid) ? 1 : 0;
-  if (a.head_dim == 64) return launch_d<64>(a, fp, bh, ntiles, stream);
-  if (a.head_dim == 128) return launch_d<128>(a, fp, bh, ntiles, stream);
+  if (a.head_dim == 64) return launch_d<64>(a, fp, stream);
+  if (a.head_dim == 128) return launch_d<128>(a, fp, stream);
   return hipErrorInvalidValue;
 }
 
