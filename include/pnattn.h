@@ -146,8 +146,9 @@ attn_status_t attn_fwd_flash_debug_s(const attn_problem_t* prob, const void* q,
                                      int32_t* s_out, void* stream);
 
 /* Bytes of workspace attn_fwd_baseline needs: S [B,H,N,N] (fp32, or int32
- * for ATTN_INT8) followed by P [B,H,N,N] (bf16 if p_bf16, else fp32).  For
- * ATTN_INT8 and ATTN_FP8, S holds the unscaled code products.            */
+ * for ATTN_INT8) followed by P [B,H,N,N] (bf16 if p_bf16, else fp32) and
+ * 256 bytes of tail padding.  For ATTN_INT8 and ATTN_FP8, S holds the
+ * unscaled code products.                                                 */
 attn_status_t attn_baseline_workspace_size(const attn_problem_t* prob,
                                            size_t* bytes);
 

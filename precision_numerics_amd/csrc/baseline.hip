@@ -18,20 +18,39 @@
 
 #include "device.hpp"
 #include "launch.hpp"
+#include "lds_dma.hpp"
 
 namespace pn {
 namespace {
 
 constexpr int kThreads = 256;
+// bytes after P in the workspace: the P.V kernel's 16-byte loads may run up
+// to 15 bytes past the last row
+constexpr size_t kWorkspaceTail = 256;
 
 // ---------------------------------------------------------------------------
 // K1: S tile of 128 queries x 128 keys per workgroup; wave w owns 32 query
-// rows and all 128 keys (4 MFMA tiles).  Operands come straight from global
-// memory (16-byte loads along d), the output leaves in 128-byte row segments.
+// rows and all 128 keys (4 MFMA tiles).  The wave's Q rows come straight
+// from global memory into registers (16-byte loads along d); the K tile is
+// loaded once per workgroup into LDS (buffer loads straight into LDS, rows
+// padded by 16 bytes so that the 32 lanes reading one 16-byte column of 32
+// rows hit distinct banks) and read from there by all four waves -- read
+// from global memory by every wave, the K rows were 2.5 bytes of L2 traffic
+// per byte of S written and the kernel's bound.  The output leaves in
+// 128-byte row segments.
 // ---------------------------------------------------------------------------
+template <int D, int QK> struct ScoresLds {
+  static constexpr int kRow = QK == 0 ? 2 * D : D;  // bytes per K row (8/16-bit codes)
+  static constexpr int kStr = kRow + 16;            // padded LDS row
+  static constexpr int kBytes = QK == 2 ? 16 : 128 * kStr;
+  static constexpr int kSeg = kBytes / 1024;
+};
+
 template <int D, int QK>  // QK: 0 bf16, 1 int8, 2 fp32, 3 E4M3 fp8
 __global__ __launch_bounds__(kThreads) void scores_kernel(const void* qp, const void* kp,
                                                          void* sp, int N, float scale) {
+  using SL = ScoresLds<D, QK>;
+  __shared__ __attribute__((aligned(1024))) char kt[SL::kBytes];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 5, n = lane & 31;
   const int64_t bh = blockIdx.z;
@@ -43,6 +62,7 @@ __global__ __launch_bounds__(kThreads) void scores_kernel(const void* qp, const 
     using T = typename std::conditional<QK == 0, uint16_t, int8_t>::type;
     constexpr int EPC = 16 / (int)sizeof(T);
     constexpr int ST = D / (2 * EPC);
+    static_assert(SL::kBytes % 1024 == 0, "the K tile is whole load segments");
     const T* Q = (const T*)qp + hoff;
     const T* K = (const T*)kp + hoff;
     i32x4 a[ST];
@@ -50,15 +70,25 @@ __global__ __launch_bounds__(kThreads) void scores_kernel(const void* qp, const 
     for (int t = 0; t < ST; ++t)
       a[t] = qi < N ? *(const i32x4*)(Q + (int64_t)qi * D + 2 * EPC * t + EPC * g)
                     : i32x4{0, 0, 0, 0};
+    // K rows j0 .. j0 + 127 into LDS (rows past N arrive as zeros through
+    // the buffer range check; their scores are not stored)
+    {
+      const i32x4 rs = buffer_rsrc(K, (uint32_t)N * SL::kRow);
+      for (int sg = wave; sg < SL::kSeg; sg += kThreads / 64)
+        lds_load16<0>(rs, seg_src_offset(sg, lane, SL::kRow, SL::kStr), (uint32_t)j0 * SL::kRow,
+                      lds_address(kt) + sg * 1024);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+    }
 #pragma unroll
     for (int jt = 0; jt < 4; ++jt) {
       const int kj = j0 + 32 * jt + n;  // B-operand column of this lane
       using Acc = typename std::conditional<QK == 1, i32x16, f32x16>::type;
       Acc acc = {};
+      const char* krow = kt + (32 * jt + n) * SL::kStr + 16 * g;
 #pragma unroll
       for (int t = 0; t < ST; ++t) {
-        const i32x4 b = kj < N ? *(const i32x4*)(K + (int64_t)kj * D + 2 * EPC * t + EPC * g)
-                               : i32x4{0, 0, 0, 0};
+        const i32x4 b = *(const i32x4*)(krow + 32 * t);
         if constexpr (QK == 0)
           acc = mfma_bf16(__builtin_bit_cast(bf16x8, a[t]), __builtin_bit_cast(bf16x8, b), acc);
         else if constexpr (QK == 1)
@@ -300,6 +330,132 @@ __global__ __launch_bounds__(kThreads) void pv_kernel(const void* pp, const void
   }
 }
 
+// ---------------------------------------------------------------------------
+// K3 for bf16 P and bf16 V: the same product O^T = V^T P^T, with the P and V
+// blocks of 64 keys streamed through two LDS buffers by buffer loads straight
+// into LDS -- block k + 1 loads while block k's products run, one barrier
+// per step.  P rows are gathered from their stride-N rows in HBM (padded by
+// 16 bytes in LDS: conflict-free 16-byte column reads of 32 rows); V rows
+// are padded by 64 bytes for the transposing reads.
+// ---------------------------------------------------------------------------
+template <int D> struct PvLds {
+  static constexpr int kBK = 64;                // keys per step
+  static constexpr int kPRow = 2 * kBK;         // bytes of a P row per step
+  static constexpr int kPStr = kPRow + 16;
+  static constexpr int kPBytes = 128 * kPStr;   // 128 query rows
+  static constexpr int kVRow = 2 * D;
+  static constexpr int kVStr = kVRow + 64;
+  static constexpr int kVBytes = kBK * kVStr;
+  static constexpr int kPSeg = kPBytes / 1024, kVSeg = kVBytes / 1024;
+  static constexpr int kPPer = (kPSeg + 3) / 4, kVPer = (kVSeg + 3) / 4;
+  static constexpr int kBuf = kPBytes + kVBytes;
+  static_assert(kPBytes % 1024 == 0 && kVBytes % 1024 == 0, "whole load segments");
+};
+
+template <int D, typename OT>
+__global__ __launch_bounds__(kThreads) void pv_bf16_kernel(const void* pp, const void* vp, void* op,
+                                                          int N) {
+  using L = PvLds<D>;
+  constexpr int DT = D / 32;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * L::kBuf];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5, n = lane & 31;
+  const int64_t bh = blockIdx.y;
+  const int q0 = blockIdx.x * 128;
+  const int rows = min(128, N - q0);
+  // P rows q0 .. q0 + rows - 1 of this head (2N bytes each); V rows of the head
+  const char* Pg = (const char*)pp + ((bh * N + q0) * (int64_t)N) * 2;
+  const char* Vg = (const char*)vp + bh * (int64_t)N * D * 2;
+  // Buffer loads check their range a dword at a time, so a 16-byte chunk
+  // crossing the end of the tile's rows would come back partly zero: the
+  // range runs to the next 16-byte boundary (the next row's first values, or
+  // the workspace's tail padding after the last row; columns past N are
+  // masked below, rows past N never stored).
+  const i32x4 rsP = buffer_rsrc(Pg, ((uint32_t)rows * (uint32_t)N * 2 + 15u) & ~15u);
+  const i32x4 rsV = buffer_rsrc(Vg, (uint32_t)N * L::kVRow);
+  // per-lane source offsets of this wave's segments (block-independent)
+  uint32_t offP[L::kPPer], offV[L::kVPer];
+#pragma unroll
+  for (int i = 0; i < L::kPPer; ++i) {
+    const int pos = ((wave + 4 * i) * 64 + lane) * 16;
+    const int r = pos / L::kPStr, c = pos % L::kPStr;
+    offP[i] = c < L::kPRow ? (uint32_t)r * (uint32_t)N * 2 + c : 0x7ffffff0u;
+  }
+#pragma unroll
+  for (int i = 0; i < L::kVPer; ++i) offV[i] = seg_src_offset(wave + 4 * i, lane, L::kVRow, L::kVStr);
+  auto issue = [&](int kb, int buf) __attribute__((always_inline)) {
+    const uint32_t base = lds_address(smem) + buf * L::kBuf + wave * 1024;
+#pragma unroll
+    for (int i = 0; i < L::kPPer; ++i)
+      if (wave + 4 * i < L::kPSeg) lds_load16<0>(rsP, offP[i], (uint32_t)kb * 2, base + i * 4096);
+#pragma unroll
+    for (int i = 0; i < L::kVPer; ++i)
+      if (wave + 4 * i < L::kVSeg)
+        lds_load16<0>(rsV, offV[i], (uint32_t)kb * L::kVRow, base + L::kPBytes + i * 4096);
+  };
+  f32x16 oacc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x16{};
+  const int vrow = 8 * g + ((lane & 15) >> 2);
+  const int vcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const int steps = (N + L::kBK - 1) / L::kBK;
+  issue(0, 0);
+  for (int st = 0; st < steps; ++st) {
+    const int kb = st * L::kBK;
+    // block st landed for every wave; every wave is done with block st - 1
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (st + 1 < steps) issue(kb + L::kBK, (st + 1) & 1);
+    const char* pl = smem + (st & 1) * L::kBuf + (32 * wave + n) * L::kPStr + 16 * g;
+    const char* vl = smem + (st & 1) * L::kBuf + L::kPBytes;
+    const bool tail = kb + L::kBK > N;  // P columns past N hold the next row's values
+#pragma unroll
+    for (int u = 0; u < L::kBK / 16; ++u) {
+      i32x4 pw = *(const i32x4*)(pl + 32 * u);
+      if (tail) {
+        // keys kb + 16u + 8g + e: zero past N (V rows there are zeros, but
+        // 0 * a non-finite P would not be)
+        const int k0 = kb + 16 * u + 8 * g;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          uint32_t w = (uint32_t)pw[e];
+          if (k0 + 2 * e >= N) w &= 0xffff0000u;
+          if (k0 + 2 * e + 1 >= N) w &= 0x0000ffffu;
+          pw[e] = (int)w;
+        }
+      }
+      const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const char* src = vl + (16 * u + vrow) * L::kVStr + (32 * dt + vcol) * 2;
+        oacc[dt] = mfma_bf16(join_bf16x8(lds_read_tr16(src), lds_read_tr16(src + 4 * L::kVStr)), pb,
+                             oacc[dt]);
+      }
+    }
+  }
+  const int q = q0 + 32 * wave + n;
+  if (q < N) {
+    OT* dst = (OT*)op + (bh * N + q) * (int64_t)D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int b4 = 0; b4 < 4; ++b4) {
+        const int d0 = 32 * dt + 8 * b4 + 4 * g;
+        const float x0 = oacc[dt][4 * b4], x1 = oacc[dt][4 * b4 + 1];
+        const float x2 = oacc[dt][4 * b4 + 2], x3 = oacc[dt][4 * b4 + 3];
+        if constexpr (sizeof(OT) == 2) {
+          uint2 w;
+          w.x = (uint32_t)f32_to_bf16(x0) | ((uint32_t)f32_to_bf16(x1) << 16);
+          w.y = (uint32_t)f32_to_bf16(x2) | ((uint32_t)f32_to_bf16(x3) << 16);
+          *(uint2*)(dst + d0) = w;
+        } else {
+          *(float4*)(dst + d0) = make_float4(x0, x1, x2, x3);
+        }
+      }
+  }
+}
+
 template <int D>
 hipError_t launch_scores(const AttnArgs& a, void* s, hipStream_t st) {
   const int N = (int)a.seq_len;
@@ -322,7 +478,15 @@ hipError_t launch_pv(const AttnArgs& a, const void* p, hipStream_t st) {
   dim3 grid((N + 127) / 128, (unsigned)(a.batch * a.heads));
   const bool vf32 = a.dtype == kF32;
   const bool of32 = vf32 || a.o_f32;  // fp32 V always gives fp32 O
-  if (a.p_bf16 && !vf32 && !of32)
+  // The streamed kernel needs 16-byte aligned P rows (N a multiple of 8);
+  // other lengths take the register-staged one, which loads unaligned rows
+  // element by element.
+  const bool aligned = N % 8 == 0;
+  if (a.p_bf16 && !vf32 && !of32 && aligned)
+    hipLaunchKernelGGL((pv_bf16_kernel<D, uint16_t>), grid, dim3(kThreads), 0, st, p, a.v, a.o, N);
+  else if (a.p_bf16 && !vf32 && aligned)
+    hipLaunchKernelGGL((pv_bf16_kernel<D, float>), grid, dim3(kThreads), 0, st, p, a.v, a.o, N);
+  else if (a.p_bf16 && !vf32 && !of32)
     hipLaunchKernelGGL((pv_kernel<D, uint16_t, uint16_t, uint16_t>), grid, dim3(kThreads), 0, st, p, a.v, a.o, N);
   else if (a.p_bf16 && !vf32)
     hipLaunchKernelGGL((pv_kernel<D, uint16_t, uint16_t, float>), grid, dim3(kThreads), 0, st, p, a.v, a.o, N);
@@ -360,7 +524,7 @@ hipError_t launch_softmax(int mode, const AttnArgs& a, const void* s, void* p, d
 
 size_t baseline_workspace_bytes(int64_t bh, int64_t n, int p_bf16) {
   const size_t elems = (size_t)bh * (size_t)n * (size_t)n;
-  return elems * 4 + elems * (p_bf16 ? 2 : 4);
+  return elems * 4 + elems * (p_bf16 ? 2 : 4) + kWorkspaceTail;
 }
 
 hipError_t launch_baseline(const AttnArgs& a, void* workspace, hipStream_t st) {

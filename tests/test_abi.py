@@ -116,10 +116,10 @@ def test_baseline_workspace_checks(clib):
     p = _prob(seq_len=100)
     n = ctypes.c_size_t(0)
     assert clib.attn_baseline_workspace_size(ctypes.byref(p), ctypes.byref(n)) == 0
-    assert n.value == 1 * 2 * 100 * 100 * (4 + 2)
+    assert n.value == 1 * 2 * 100 * 100 * (4 + 2) + 256   # S, P, tail padding
     p32 = _prob(seq_len=100, p_bf16=0)
     assert clib.attn_baseline_workspace_size(ctypes.byref(p32), ctypes.byref(n)) == 0
-    assert n.value == 1 * 2 * 100 * 100 * 8
+    assert n.value == 1 * 2 * 100 * 100 * 8 + 256
     rc = clib.attn_fwd_baseline(ctypes.byref(p), FAKE, FAKE, FAKE, None, None, FAKE, 100, FAKE,
                                 None)
     assert rc == B.ATTN_ERR_WORKSPACE
