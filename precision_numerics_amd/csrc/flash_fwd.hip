@@ -228,6 +228,11 @@ constexpr int kSchedDsRead = 0x0100;
 // s_waitcnt immediate (gfx9 encoding) for vmcnt(0) with expcnt and lgkmcnt
 // left at their maxima: wait for this wave's outstanding vector-memory ops.
 constexpr int kWaitVmcnt0 = 0x0F70;
+// the same for vmcnt(n): all but this wave's n most recent vector-memory
+// operations done (they complete in issue order)
+constexpr int wait_vmcnt(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+// dword 3 of a raw buffer resource (as buffer_rsrc builds it)
+constexpr int kRsrcWord3 = 0x00020000;
 
 // Wave priority (s_setprio) while a wave issues its matrix products.
 constexpr int kPrioMfma = 2;
@@ -395,7 +400,7 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
   i32x4 qv[QK == QK_F32 ? 1 : QST];
   float qf[QK == QK_F32 ? QST : 1];
   float sq_log2 = 0.f;  // this tile's row scale times scale * log2(e) (8-bit Q/K)
-  float sq_pend = 0.f;  // the same for the tile whose Q rows were loaded last
+  float sq_pend = 0.f;  // the row scale (unscaled) of the tile whose Q rows were loaded last
   // load the Q row of query `row` of head `b` (zeros past the sequence end)
   auto load_q = [&](int b, int row) __attribute__((always_inline)) {
     const bool ok = row < N;
@@ -404,17 +409,32 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
 #pragma unroll
       for (int t = 0; t < QST; ++t) qf[t] = ok ? Qg[(int64_t)row * D + 2 * t + g] : 0.f;
     } else {
+      // Range-checked buffer loads, issued by every lane whatever its row
+      // (a row past the sequence end starts at the end of the range and
+      // reads zeros): each wave issues exactly kQLoads vector-memory
+      // instructions here, which the counted wait at a tile switch relies on.
       constexpr int EPC = 16 / (int)sizeof(QT);  // elements per 16-byte chunk
+      const uint32_t rowc = (uint32_t)(ok ? row : N);
+      const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)Qg, (short)0, (int)((uint32_t)N * D * sizeof(QT)), kRsrcWord3);
 #pragma unroll
-      for (int t = 0; t < QST; ++t) {
-        const QT* src = Qg + (int64_t)row * D + 2 * EPC * t + EPC * g;
-        qv[t] = ok ? *(const i32x4*)src : i32x4{0, 0, 0, 0};
+      for (int t = 0; t < QST; ++t)
+        qv[t] = __builtin_amdgcn_raw_buffer_load_b128(
+            rq, (int)((rowc * D + 2 * EPC * t + EPC * g) * sizeof(QT)), 0, 0);
+      if constexpr (kScaledQK<QK>) {
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(p.q_scale + (int64_t)b * N), (short)0, (int)((uint32_t)N * 4), kRsrcWord3);
+        // used only once the tile becomes current (a use here would wait
+        // for the load at once)
+        sq_pend = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, (int)(rowc * 4), 0, 0));
       }
-      if constexpr (kScaledQK<QK>) sq_pend = ok ? p.q_scale[(int64_t)b * N + row] * p.scale_log2 : 0.f;
     }
   };
+  // vector-memory instructions of one load_q (none counted for fp32 Q, whose
+  // loads are waited for in full)
+  constexpr int kQLoads = QK == QK_F32 ? -1 : QST + (kScaledQK<QK> ? 1 : 0);
   load_q(bh, qrow);
-  sq_log2 = sq_pend;
+  sq_log2 = sq_pend * p.scale_log2;
 
   // One wait for the Q row and the first K tile, with a wait the compiler
   // sees: otherwise its wait-count pass, unsure the Q loads finished before
@@ -1016,16 +1036,34 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
     q0w = cur.q0 + wave * 32;
     qrow = q0w + n;
     qvalid = qrow < N;
-    sq_log2 = sq_pend;
+    sq_log2 = sq_pend * p.scale_log2;
   };
 
+  // end of group 0's X_j: the K loads issued in M_j (and any O stores) are
+  // awaited; after the last X of a tile, which loads the next tile's Q rows,
+  // those Q loads stay in flight (they are awaited at the end of M_n).
+  // Top of a block loop.  Nothing is in flight here on any path that
+  // reaches it (the last X of a tile, which leaves the next tile's Q loads in
+  // flight, also leaves the loop), but the compiler cannot tell: without this
+  // wait it assumes those Q loads may be pending and waits for them before
+  // the S products, and since it does not count the buffer->LDS loads, that
+  // wait would also cover the K/V loads issued earlier in the same half-step.
+  auto loop_top_wait = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  };
+  auto wait_x0 = [&](int j) __attribute__((always_inline)) {
+    if (kQLoads >= 0 && j == cur.nblk - 1 && nxt.valid)
+      __builtin_amdgcn_s_waitcnt(wait_vmcnt(kQLoads < 0 ? 0 : kQLoads));
+    else
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  };
   if (group == 0) {
     while (true) {
       m_body(0, jg0, kNo, kYes, kIssueK, next_k(0));
       block_barrier();
       x_prologue(0);
       half_x(0);
-      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      wait_x0(0);
       block_barrier();
       // Causal tiles: when the last key block lies wholly above group 0's
       // rows (the tile's first half), every score of it is masked for this
@@ -1036,22 +1074,25 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
       const int nb = cur.nblk;
       const bool skip_last = CAUSAL && nb >= 2 && (nb - 1) * BC > cur.q0 + kBR / 2 - 1;
       for (int j = 1; j < nb - (skip_last ? 1 : 0); ++j) {
+        loop_top_wait();
         m_body(j, jg0 + j, kYes, kYes, kIssueK, next_k(j));
         block_barrier();
         x_prologue(j);
         half_x(j);
-        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        wait_x0(j);
         block_barrier();
       }
       if (skip_last) {
         m_body(nb - 1, jg0 + nb - 1, kYes, kNo, kIssueK, next_k(nb - 1));
         block_barrier();
         x_prologue(nb - 1);
-        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        wait_x0(nb - 1);
         block_barrier();
       } else {
         m_body(nb, jg0 + nb, kYes, kNo, kIssueNone, kNone);
       }
+      // the next tile's Q rows (loaded in the last X) before its S products
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
       block_barrier();
       const bool more = nxt.valid;
       advance();
@@ -1069,6 +1110,7 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
       half_x(0);
       block_barrier();
       for (int j = 1; j < cur.nblk; ++j) {
+        loop_top_wait();
         m_body(j, jg0 + j, kYes, kYes, kIssueV, this_v(j));
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         block_barrier();
@@ -1077,6 +1119,11 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
         block_barrier();
       }
       m_body(cur.nblk, jg0 + cur.nblk, kYes, kNo, kIssueNone, kNone);
+      // The next tile's Q rows (loaded in the last X) are awaited here, with
+      // no load in flight behind them; otherwise the compiler waits for them
+      // at their first use in the next M_0, which by then has issued that
+      // tile's first V block, and the wait would cover it too.
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
       block_barrier();
       const bool more = nxt.valid;
       advance();
