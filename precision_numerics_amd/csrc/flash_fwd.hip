@@ -103,9 +103,10 @@ template <int D, int QK, int PV> struct Tile {
   static constexpr int kSegVPerWave = (kSegV + kIssuers - 1) / kIssuers;
   static constexpr int kSegPerWave = kSegKPerWave > kSegVPerWave ? kSegKPerWave : kSegVPerWave;
   static constexpr int kBytesSk = kScaledQK<QK> ? kBC * 4 : 0;
-  // [K buf0][K buf1][V buf0][V buf1][sk buf0][sk buf1][sk buf2].  The key
-  // scales of block j are read in the softmax half-step X_j, which group 1
-  // runs while group 0 already loads block j + 2: they take three buffers.
+  // [K buf0][K buf1][V buf0][V buf1][sk buf0][sk buf1][sk buf2].  The fp8
+  // key scales of block j are read in the softmax half-step X_j, which
+  // group 1 runs while group 0 already loads block j + 2: they take three
+  // buffers (int8 reads them earlier, in M_j).
   static constexpr int kOffV = 2 * kBytesK;
   static constexpr int kOffSk = kOffV + 2 * kBytesV;
   static constexpr int kLds = kOffSk + 3 * kBytesSk;
@@ -510,6 +511,11 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
   // softmax half-step.
   constexpr bool kFenced = PV == PV_BF16 && (QK == QK_BF16 || kScaledQK<QK>);
   constexpr bool kScaleInX = kFenced && kScaledQK<QK>;
+  // where the key scales are applied (the row scale always enters with the
+  // exp2 argument): int8 at the end of the matrix half-step, after the exact
+  // int32 -> fp32 conversion (0.8 % faster on c5), fp8 in the softmax
+  // half-step (2.5 % faster there than in the matrix half-step)
+  constexpr bool kScaleInM = kScaleInX && QK == QK_I8;
   auto fresh_voff = [&](uint32_t (&dst)[TL::kSegPerWave]) __attribute__((always_inline)) {
     int l = lane;
     asm volatile("" : "+v"(l));
@@ -546,8 +552,10 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
       // instruction sits in this stream: the wave sharing the SIMD runs a
       // dense VALU stream meanwhile, and an in-order wave whose VALU
       // instruction waits for the VALU port also holds back the products
-      // behind it.
-      constexpr int kAhead = 8;
+      // behind it.  Four products ahead (~130 cycles) already cover the LDS
+      // latency; at d = 128 the registers eight would hold cost spills, at
+      // d = 64 eight measure faster.
+      constexpr int kAhead = D == 128 ? 4 : 8;
       constexpr int NPV = DO_PV ? DT * (BC / 16) : 0;  // P.V products, u-major
       constexpr int NSM = DO_S ? NKS * QST : 0;        // S products, chain by chain
       const char* vl = (const char*)smem + TL::kOffV + ((jg - 1) & 1) * TL::kBytesV + v_lane;
@@ -625,8 +633,7 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
       }
       if constexpr (DO_S && QK == QK_I8) {
         // exact int32 -> fp32 (|products| < 2^24) while the other wave of the
-        // SIMD still runs its softmax; the key scales follow in this
-        // wave's softmax half-step
+        // SIMD still runs its softmax
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
           const i32x16 si = __builtin_bit_cast(i32x16, s[ks]);  // whole-vector cast
@@ -634,9 +641,27 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
           for (int r = 0; r < 16; ++r) s[ks][r] = (float)si[r];
         }
       }
+      if constexpr (DO_S && kScaleInM) {
+        // t = code product * key scale, here rather than in the softmax
+        // half-step, which bounds the 8-bit steps (the matrix half-step has
+        // the slack: its score products are half as many instructions)
+        const float* skt = (const float*)(smem + TL::kOffSk + (jg % 3) * TL::kBytesSk);
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+          const f32x4 a0 = *(const f32x4*)(skt + 32 * ks + 8 * g);
+          const f32x4 a1 = *(const f32x4*)(skt + 32 * ks + 8 * g + 4);
+          const f32x4 b0 = *(const f32x4*)(skt + 32 * ks + 16 + 8 * g);
+          const f32x4 b1 = *(const f32x4*)(skt + 32 * ks + 16 + 8 * g + 4);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float sk = r < 4 ? a0[r] : r < 8 ? a1[r - 4] : r < 12 ? b0[r - 8] : b1[r - 12];
+            s[ks][r] *= sk;
+          }
+        }
+      }
       if constexpr (DO_S) {
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) pin(s[ks]);  // raw q.k; scaled inside exp2
+        for (int ks = 0; ks < NKS; ++ks) pin(s[ks]);  // q.k (int8: times the key scale)
       }
       if constexpr (DO_PV) {
 #pragma unroll
@@ -783,7 +808,7 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
   // ================= X_j: online softmax of block j
   auto half_x = [&](const int j) __attribute__((always_inline)) {
     const int kb = j * BC;
-    if constexpr (kScaleInX) {
+    if constexpr (kScaleInX && !kScaleInM) {
       // t = code product * key scale; the row's scale enters with the exp2
       // argument (it is positive, so the row max is taken on t).  The
       // products are fp32 here (int8: converted in the matrix step).
