@@ -965,29 +965,48 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
   auto finish = [&](int b, int row) __attribute__((always_inline)) {
     const float l_tot = pair32_sum(l_run);
     const float inv = 1.f / l_tot;
-    if (row < N) {
-      const int64_t base = (int64_t)b * N * D + (int64_t)row * D;
-      // O in fp32 (fp32 V, or asked for: a separate instance, so that the
-      // bf16-output kernels carry no trace of it)
-      constexpr bool f32out = sizeof(VT) == 4 || OF32;
+    const int64_t base = (int64_t)b * N * D + (int64_t)row * D;
+    // O in fp32 (fp32 V, or asked for: a separate instance, so that the
+    // bf16-output kernels carry no trace of it)
+    constexpr bool f32out = sizeof(VT) == 4 || OF32;
+    if constexpr (f32out) {
+      if (row < N) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int b4 = 0; b4 < 4; ++b4) {
+            const int d0 = 32 * dt + 8 * b4 + 4 * g;
+            *(float4*)((float*)p.o + base + d0) =
+                make_float4(oacc[dt][4 * b4 + 0] * inv, oacc[dt][4 * b4 + 1] * inv,
+                            oacc[dt][4 * b4 + 2] * inv, oacc[dt][4 * b4 + 3] * inv);
+          }
+      }
+    } else {
+      // Lane (n, g) holds, for each 8-column group b4 of a 32-column
+      // subtile, columns 4g..4g+3 of row n (8 bytes once in bf16).  One
+      // permlane32 swap per dword pairs the groups up: afterwards lane g
+      // holds all eight columns of group 2k + g, so each store writes 16
+      // bytes (half the store instructions of 8-byte pieces).  Both lanes
+      // of a pair serve the same row, and the swaps run before the row
+      // test, with every lane active.
+      auto pk = [&](int dt, int r) __attribute__((always_inline)) {
+        return (uint32_t)f32_to_bf16(oacc[dt][r] * inv) |
+               ((uint32_t)f32_to_bf16(oacc[dt][r + 1] * inv) << 16);
+      };
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int b4 = 0; b4 < 4; ++b4) {
-          const int d0 = 32 * dt + 8 * b4 + 4 * g;
-          const float x0 = oacc[dt][4 * b4 + 0] * inv, x1 = oacc[dt][4 * b4 + 1] * inv;
-          const float x2 = oacc[dt][4 * b4 + 2] * inv, x3 = oacc[dt][4 * b4 + 3] * inv;
-          if constexpr (f32out) {
-            *(float4*)((float*)p.o + base + d0) = make_float4(x0, x1, x2, x3);
-          } else {
-            uint2 w;
-            w.x = (uint32_t)f32_to_bf16(x0) | ((uint32_t)f32_to_bf16(x1) << 16);
-            w.y = (uint32_t)f32_to_bf16(x2) | ((uint32_t)f32_to_bf16(x3) << 16);
-            *(uint2*)((uint16_t*)p.o + base + d0) = w;
-          }
+        for (int k = 0; k < 2; ++k) {
+          // group 2k (X) and 2k + 1 (Y), two dwords each
+          const auto s0 = __builtin_amdgcn_permlane32_swap(pk(dt, 8 * k + 0), pk(dt, 8 * k + 4), false, false);
+          const auto s1 = __builtin_amdgcn_permlane32_swap(pk(dt, 8 * k + 2), pk(dt, 8 * k + 6), false, false);
+          if (row < N)
+            *(uint4*)((uint16_t*)p.o + base + 32 * dt + 16 * k + 8 * g) =
+                make_uint4(s0[0], s1[0], s0[1], s1[1]);
         }
-      if (p.lse != nullptr && g == 0) p.lse[(int64_t)b * N + row] = (m_run + __log2f(l_tot)) * kLn2;
     }
+    if (row < N && p.lse != nullptr && g == 0)
+      p.lse[(int64_t)b * N + row] = (m_run + __log2f(l_tot)) * kLn2;
     m_run = -INFINITY;
     mraw_run = -INFINITY;
     l_run = 0.f;
