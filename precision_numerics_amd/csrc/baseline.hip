@@ -39,6 +39,25 @@ constexpr size_t kWorkspaceTail = 256;
 // per byte of S written and the kernel's bound.  The output leaves in
 // 128-byte row segments.
 // ---------------------------------------------------------------------------
+// Workgroup -> (head, tile of the head).  Workgroups go to the eight XCDs in
+// turn (linear dispatch index mod 8); when the head count is a multiple of
+// eight, head 8c + x takes the slots c*T .. (c+1)*T - 1 of XCD x, so every
+// tile of a head runs on one XCD and the K and V rows its tiles share are
+// fetched from HBM into that XCD's L2 once (in dispatch order the tiles of
+// a head would go to all eight).  Any other head count: head-major order.
+__device__ __forceinline__ void head_tile(int64_t tiles_per_head, int64_t heads, int64_t& head,
+                                          int64_t& tile) {
+  const int64_t L = blockIdx.x + (int64_t)gridDim.x * (blockIdx.y + (int64_t)gridDim.y * blockIdx.z);
+  if (heads % 8 == 0) {
+    const int64_t i = L >> 3;
+    head = (i / tiles_per_head) * 8 + (L & 7);
+    tile = i % tiles_per_head;
+  } else {
+    head = L / tiles_per_head;
+    tile = L % tiles_per_head;
+  }
+}
+
 template <int D, int QK> struct ScoresLds {
   static constexpr int kRow = QK == 0 ? 2 * D : D;  // bytes per K row (8/16-bit codes)
   static constexpr int kStr = kRow + 16;            // padded LDS row
@@ -53,9 +72,10 @@ __global__ __launch_bounds__(kThreads) void scores_kernel(const void* qp, const 
   __shared__ __attribute__((aligned(1024))) char kt[SL::kBytes];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 5, n = lane & 31;
-  const int64_t bh = blockIdx.z;
-  const int i0 = blockIdx.y * 128 + wave * 32;
-  const int j0 = blockIdx.x * 128;
+  int64_t bh, tile;
+  head_tile((int64_t)gridDim.x * gridDim.y, gridDim.z, bh, tile);
+  const int i0 = (int)(tile / gridDim.x) * 128 + wave * 32;
+  const int j0 = (int)(tile % gridDim.x) * 128;
   const int64_t hoff = bh * (int64_t)N * D;
   const int qi = i0 + n;  // A-operand row of this lane
   if constexpr (QK == 0 || QK == 1 || QK == 3) {
@@ -102,12 +122,14 @@ __global__ __launch_bounds__(kThreads) void scores_kernel(const void* qp, const 
           const int i = i0 + 8 * (r >> 2) + 4 * g + (r & 3);
           if (i < N) {
             const int64_t off = (bh * N + i) * (int64_t)N + kj;
+            // S is written once and read once, far beyond any cache:
+            // non-temporal stores
             if constexpr (QK == 0)
-              ((float*)sp)[off] = acc[r] * scale;
+              __builtin_nontemporal_store(acc[r] * scale, (float*)sp + off);
             else if constexpr (QK == 1)
-              ((int32_t*)sp)[off] = acc[r];
+              __builtin_nontemporal_store((int32_t)acc[r], (int32_t*)sp + off);
             else
-              ((float*)sp)[off] = acc[r];  // unscaled; K2 applies the row scales
+              __builtin_nontemporal_store((float)acc[r], (float*)sp + off);  // unscaled; K2 applies the row scales
           }
         }
       }
@@ -172,19 +194,22 @@ __global__ __launch_bounds__(kThreads) void softmax_kernel(const void* sp, void*
   const int64_t row = (bh * N + i) * (int64_t)N;
   const int jend = causal ? i + 1 : N;  // visible keys: j < jend
   const float sqc = SMODE != 0 ? q_scale[bh * N + i] * scale : 0.f;
+  // S: read once (non-temporal)
   auto score = [&](int j) -> float {
     if constexpr (SMODE == 1)
-      return (float)((const int32_t*)sp)[row + j] * (k_scale[bh * N + j] * sqc);
+      return (float)__builtin_nontemporal_load((const int32_t*)sp + row + j) *
+             (k_scale[bh * N + j] * sqc);
     else if constexpr (SMODE == 2)
-      return ((const float*)sp)[row + j] * (k_scale[bh * N + j] * sqc);
+      return __builtin_nontemporal_load((const float*)sp + row + j) * (k_scale[bh * N + j] * sqc);
     else
-      return ((const float*)sp)[row + j];
+      return __builtin_nontemporal_load((const float*)sp + row + j);
   };
   auto store = [&](int j, float pv) {
+    // P: written once, read once by K3 (non-temporal)
     if constexpr (PBF16)
-      ((uint16_t*)pp)[row + j] = f32_to_bf16(pv);
+      __builtin_nontemporal_store(f32_to_bf16(pv), (uint16_t*)pp + row + j);
     else
-      ((float*)pp)[row + j] = pv;
+      __builtin_nontemporal_store(pv, (float*)pp + row + j);
   };
   float m = -INFINITY;
   if constexpr (CACHE > 0) {
@@ -241,8 +266,9 @@ __global__ __launch_bounds__(kThreads) void pv_kernel(const void* pp, const void
   __shared__ __attribute__((aligned(16))) VT v_lds[64 * VS];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, n = lane & 31;
-  const int64_t bh = blockIdx.y;
-  const int q0 = blockIdx.x * 128;
+  int64_t bh, tile;
+  head_tile(gridDim.x, gridDim.y, bh, tile);
+  const int q0 = (int)tile * 128;
   const PT* P = (const PT*)pp + bh * (int64_t)N * N;
   const VT* V = (const VT*)vp + bh * (int64_t)N * D;
   f32x16 oacc[DT];
@@ -361,8 +387,9 @@ __global__ __launch_bounds__(kThreads) void pv_bf16_kernel(const void* pp, const
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, n = lane & 31;
-  const int64_t bh = blockIdx.y;
-  const int q0 = blockIdx.x * 128;
+  int64_t bh, tile;
+  head_tile(gridDim.x, gridDim.y, bh, tile);
+  const int q0 = (int)tile * 128;
   const int rows = min(128, N - q0);
   // P rows q0 .. q0 + rows - 1 of this head (2N bytes each); V rows of the head
   const char* Pg = (const char*)pp + ((bh * N + q0) * (int64_t)N) * 2;
