@@ -529,11 +529,26 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
                     const Prefetch& rq) __attribute__((always_inline)) {
     constexpr bool DO_PV = decltype(do_pv_c)::value;
     constexpr bool DO_S = decltype(do_s_c)::value;
-    // loads to issue: 0 none, 1 K (spread over the products), 2 V (all
-    // before the first product)
+    // loads to issue: 0 none, 1 K (spread over the products), 2 V (before
+    // the first product, or spread over the first half of the products)
     constexpr int ISSUE = decltype(issue_c)::value;
     constexpr int NSEG = TL::kSegKPerWave;
-    if constexpr (ISSUE == 2) {
+    // At d = 128 group 1's V loads are spread over the first half of its
+    // fenced products: issued back to back they delay the first product by
+    // their issue time (about 240 cycles), while the last one still has half
+    // the half-step to land before the wait at its end.  (At d = 64 the
+    // half-step is too short for that: back to back measures faster.)
+    constexpr bool kSpreadV = kFenced && !kFreshVoff && D == 128;
+    constexpr int NSEGV = TL::kSegVPerWave;
+    i32x4 rsV = {0, 0, 0, 0};
+    uint32_t vsoff = 0, vlds = 0;
+    if constexpr (ISSUE == 2 && kSpreadV) {
+      rsV = uniform(buffer_rsrc(rq.base, (uint32_t)N * TL::kRowV));
+      vsoff = __builtin_amdgcn_readfirstlane((uint32_t)rq.kb * TL::kRowV);
+      vlds = __builtin_amdgcn_readfirstlane(lds_address(smem) + TL::kOffV + rq.buf * TL::kBytesV +
+                                            wg * 1024);
+    }
+    if constexpr (ISSUE == 2 && !kSpreadV) {
       if constexpr (!kFreshVoff) {
         if (rq.on) issue_v<D, QK, PV>(smem, wg, rq.kb, rq.buf, rq.base, N, voff);
       } else {
@@ -610,6 +625,14 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
           static_for<NSEG>([&](auto qc) __attribute__((always_inline)) {
             constexpr int q = decltype(qc)::value;
             if ((2 * q + 1) * (NPV + NSM) / (2 * NSEG) == i) issue_one(qc, rq);
+          });
+        }
+        if constexpr (ISSUE == 2 && kSpreadV) {
+          static_for<NSEGV>([&](auto qc) __attribute__((always_inline)) {
+            constexpr int q = decltype(qc)::value;
+            if ((2 * q + 1) * (NPV + NSM) / (4 * NSEGV) == i && rq.on &&
+                (TL::kSegV % TL::kIssuers == 0 || wg + q * TL::kIssuers < TL::kSegV))
+              lds_load16<q * TL::kIssuers * 1024>(rsV, voff[q], vsoff, vlds);
           });
         }
       }
