@@ -56,7 +56,7 @@ LEG_SETTLE_S = 0.1
 
 # HBM bytes per launch of the flash kernel on c3, from two rocprofv3 --pmc
 # passes (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch).  A plain 256 MiB
-# device copy reads FETCH_SIZE = 131084 KiB and WRITE_SIZE = 262144 KiB, so
+# device copy reads FETCH_SIZE = 131085 KiB and WRITE_SIZE = 262144 KiB, so
 # FETCH_SIZE is scaled by 2 and WRITE_SIZE by 1 (the copy's and the flash
 # kernel's reads are all 128-byte requests, TCC_EA0_RDREQ_128B, which the
 # FETCH_SIZE formula counts as 64 bytes).  The figure is valid only for the
@@ -67,8 +67,8 @@ TRAFFIC_SOURCES = ("precision_numerics_amd/csrc/flash_fwd.hip",
                    "precision_numerics_amd/csrc/lds_dma.hpp")
 TRAFFIC = {
     "workload": "c3",
-    "sources_sha256": "1572ecee310c6703fc2f25ee5c96ebe703e9f4f66209635591bfd4d8a01936a4",
-    "fetch_kib": 302341.0, "fetch_scale": 2.0,
+    "sources_sha256": "d5b8a907e35003ed393ab8f4b1fc33b58473113d4758866cf695237d96ad3230",
+    "fetch_kib": 305967.0, "fetch_scale": 2.0,
     "write_kib": 131072.0, "write_scale": 1.0,
 }
 
