@@ -25,7 +25,9 @@
 //    SIMD issues its matrix products (P_{j-1} V_{j-1}, then S_j) the other
 //    does its softmax arithmetic (mask, max, exp, sums, the rescale of O by
 //    exp(m - m'), P -> bf16) on VALU: the two instruction streams overlap
-//    on each SIMD, and the matrix half-step holds no VALU instruction.
+//    on each SIMD, and the matrix half-step holds no VALU instruction
+//    (int8 aside: its scores are converted to fp32 and take their key
+//    scales at the end of it).
 //  * The wave computes S^T = K_j Q^T (32 keys x 32 queries per MFMA tile), so
 //    lane l owns query l%32 and half of the block's keys: the row max and row
 //    sum are in-lane reductions plus one permlane32_swap, and exp(m - m') is
