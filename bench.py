@@ -67,7 +67,7 @@ TRAFFIC_SOURCES = ("precision_numerics_amd/csrc/flash_fwd.hip",
                    "precision_numerics_amd/csrc/lds_dma.hpp")
 TRAFFIC = {
     "workload": "c3",
-    "sources_sha256": "d5b8a907e35003ed393ab8f4b1fc33b58473113d4758866cf695237d96ad3230",
+    "sources_sha256": "261308b80292d5f5d8e1c3db683bf2b719406df32d447bc7fe4a77e1d1d59377",
     "fetch_kib": 305967.0, "fetch_scale": 2.0,
     "write_kib": 131072.0, "write_scale": 1.0,
 }
