@@ -10,8 +10,8 @@ tile the arithmetic is the same either way, so
 * the heads of a persistent launch are bitwise equal to the same heads run
   alone (one tile per workgroup).
 
-Shapes are ragged (N not a multiple of the 256-row tile or the key block);
-head counts select both tile orders (grouped by four heads per XCD when
+Shapes are ragged (N not a multiple of the 256-row tile or the key block),
+some with a single key block per tile; head counts select both tile orders (grouped by four heads per XCD when
 batch*heads is a multiple of 32, plain otherwise).
 """
 from __future__ import annotations
@@ -97,6 +97,12 @@ CASES = [
     ("c5", 64, True, True, 300, False),
     ("c1", 64, True, False, 600, True),
     ("c5-fp8", 128, True, True, 520, False),
+    # one key block per tile (N <= 128): the softmax half-step that finishes
+    # the previous tile also loads the next tile's Q rows, so the counted
+    # wait there follows the O stores
+    ("c3", 128, True, True, 100, False),
+    ("c5", 128, False, True, 128, True),
+    ("c5-fp8", 64, True, True, 77, True),
 ]
 
 
