@@ -67,8 +67,8 @@ TRAFFIC_SOURCES = ("precision_numerics_amd/csrc/flash_fwd.hip",
                    "precision_numerics_amd/csrc/lds_dma.hpp")
 TRAFFIC = {
     "workload": "c3",
-    "sources_sha256": "261308b80292d5f5d8e1c3db683bf2b719406df32d447bc7fe4a77e1d1d59377",
-    "fetch_kib": 305967.0, "fetch_scale": 2.0,
+    "sources_sha256": "d693a235d92deea6f3dedb33172ce45ce7e5e28e8034985e768f6c9dd70127eb",
+    "fetch_kib": 306694.0, "fetch_scale": 2.0,
     "write_kib": 131072.0, "write_scale": 1.0,
 }
 

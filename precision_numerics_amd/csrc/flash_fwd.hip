@@ -574,11 +574,14 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
       // d = 64 eight measure faster.
       constexpr int kAhead = D == 128 ? 4 : 8;
       constexpr int NPV = DO_PV ? DT * (BC / 16) : 0;  // P.V products, u-major
-      constexpr int NSM = DO_S ? NKS * QST : 0;        // S products, chain by chain
+      // fp8: one 32x32x64 product takes two 16-byte chunks of the row
+      constexpr int SPC = QK == QK_F8 ? 2 : 1;         // chunks per S product
+      constexpr int QSP = QST / SPC;                   // S products per 32-key subtile
+      constexpr int NSM = DO_S ? NKS * QSP : 0;        // S products, chain by chain
       const char* vl = (const char*)smem + TL::kOffV + ((jg - 1) & 1) * TL::kBytesV + v_lane;
       const char* k0 = (const char*)smem + (jg & 1) * TL::kBytesK + k_lane + 16 * g;
       i16x4 vlo[NPV > 0 ? NPV : 1], vhi[NPV > 0 ? NPV : 1];
-      i32x4 kf[NSM > 0 ? NSM : 1];
+      i32x4 kf[NSM > 0 ? NSM : 1][SPC];
       // the S products accumulate straight into the score registers X
       // reads (a separate accumulator made the compiler copy all of them)
       if constexpr (DO_S) {
@@ -592,7 +595,9 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
           vhi[i] = lds_read_tr16(src + 4 * TL::kStrV);
         } else {
           const int t = i - NPV;
-          kf[t] = *(const i32x4*)(k0 + (t / QST) * 32 * TL::kStrK + 32 * (t % QST));
+#pragma unroll
+          for (int c = 0; c < SPC; ++c)
+            kf[t][c] = *(const i32x4*)(k0 + (t / QSP) * 32 * TL::kStrK + 32 * ((t % QSP) * SPC + c));
         }
       };
       auto product = [&](const int i) __attribute__((always_inline)) {
@@ -603,13 +608,14 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
           // half-step applies the key scales
           const int t = i - NPV;
           if constexpr (QK == QK_BF16)
-            s[t / QST] = mfma_bf16(__builtin_bit_cast(bf16x8, kf[t]),
+            s[t / QST] = mfma_bf16(__builtin_bit_cast(bf16x8, kf[t][0]),
                                    __builtin_bit_cast(bf16x8, qv[t % QST]), s[t / QST]);
           else if constexpr (QK == QK_I8)
             s[t / QST] = __builtin_bit_cast(
-                f32x16, mfma_i8(kf[t], qv[t % QST], __builtin_bit_cast(i32x16, s[t / QST])));
+                f32x16, mfma_i8(kf[t][0], qv[t % QST], __builtin_bit_cast(i32x16, s[t / QST])));
           else
-            s[t / QST] = mfma_fp8x2(kf[t], qv[t % QST], s[t / QST]);
+            s[t / QSP] = mfma_fp8x4(kf[t][0], kf[t][1], qv[(t % QSP) * 2], qv[(t % QSP) * 2 + 1],
+                                    s[t / QSP]);
         }
       };
       // The wave sharing this SIMD runs its softmax meanwhile; a dense VALU
