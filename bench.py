@@ -67,7 +67,7 @@ TRAFFIC_SOURCES = ("precision_numerics_amd/csrc/flash_fwd.hip",
                    "precision_numerics_amd/csrc/lds_dma.hpp")
 TRAFFIC = {
     "workload": "c3",
-    "sources_sha256": "d693a235d92deea6f3dedb33172ce45ce7e5e28e8034985e768f6c9dd70127eb",
+    "sources_sha256": "7b68e17d1584ff10c166519336dcd55ca6311a733b545792ad3b5ec9e4884e06",
     "fetch_kib": 306694.0, "fetch_scale": 2.0,
     "write_kib": 131072.0, "write_scale": 1.0,
 }

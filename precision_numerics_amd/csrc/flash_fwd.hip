@@ -26,8 +26,8 @@
 //    does its softmax arithmetic (mask, max, exp, sums, the rescale of O by
 //    exp(m - m'), P -> bf16) on VALU: the two instruction streams overlap
 //    on each SIMD, and the matrix half-step holds no VALU instruction
-//    (int8 aside: its scores are converted to fp32 and take their key
-//    scales at the end of it).
+//    (8-bit Q/K aside: their scores take their key scales at the end of it,
+//    int8's after the exact conversion to fp32).
 //  * The wave computes S^T = K_j Q^T (32 keys x 32 queries per MFMA tile), so
 //    lane l owns query l%32 and half of the block's keys: the row max and row
 //    sum are in-lane reductions plus one permlane32_swap, and exp(m - m') is
@@ -500,32 +500,15 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
     }
   };
 
-  // The fp8 engine runs out of registers when the source offsets of this
-  // wave's segments stay live through the loop: the compiler then spills
-  // them, and each reload's wait also waits for the loads already in flight.
-  // There they are recomputed at the point of use (the opaque lane keeps the
-  // computation from being hoisted back out); the other engines keep them,
-  // since the recomputation costs vector instructions in the matrix
-  // half-step.
-  constexpr bool kFreshVoff = QK == QK_F8;
   // The fenced matrix half-step (products and LDS reads only) serves bf16 P
-  // with bf16, int8 or fp8 Q/K; 8-bit scores get their key scales in the
-  // softmax half-step.
+  // with bf16, int8 or fp8 Q/K.
   constexpr bool kFenced = PV == PV_BF16 && (QK == QK_BF16 || kScaledQK<QK>);
+  // 8-bit scores in the fenced half-step take their key scales at the end
+  // of it (after the exact int32 -> fp32 conversion for int8) and their row
+  // scale with the exp2 argument.  In the softmax half-step, whose vector
+  // work bounds the 8-bit steps, the key scales measured 0.8 % (int8) and
+  // 5.6 % (fp8) slower on c5.
   constexpr bool kScaleInX = kFenced && kScaledQK<QK>;
-  // where the key scales are applied (the row scale always enters with the
-  // exp2 argument): int8 at the end of the matrix half-step, after the exact
-  // int32 -> fp32 conversion (0.8 % faster on c5), fp8 in the softmax
-  // half-step (2.5 % faster there than in the matrix half-step)
-  constexpr bool kScaleInM = kScaleInX && QK == QK_I8;
-  auto fresh_voff = [&](uint32_t (&dst)[TL::kSegPerWave]) __attribute__((always_inline)) {
-    int l = lane;
-    asm volatile("" : "+v"(l));
-#pragma unroll
-    for (int i = 0; i < TL::kSegPerWave; ++i)
-      dst[i] = group == 0 ? seg_src_offset(wg + i * TL::kIssuers, l, TL::kRowK, TL::kStrK)
-                          : seg_src_offset(wg + i * TL::kIssuers, l, TL::kRowV, TL::kStrV);
-  };
 
   auto m_body = [&](const int jl, const int jg, auto do_pv_c, auto do_s_c, auto issue_c,
                     const Prefetch& rq) __attribute__((always_inline)) {
@@ -540,7 +523,7 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
     // their issue time (about 240 cycles), while the last one still has half
     // the half-step to land before the wait at its end.  (At d = 64 the
     // half-step is too short for that: back to back measures faster.)
-    constexpr bool kSpreadV = kFenced && !kFreshVoff && D == 128;
+    constexpr bool kSpreadV = kFenced && D == 128;
     constexpr int NSEGV = TL::kSegVPerWave;
     i32x4 rsV = {0, 0, 0, 0};
     uint32_t vsoff = 0, vlds = 0;
@@ -551,13 +534,7 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
                                             wg * 1024);
     }
     if constexpr (ISSUE == 2 && !kSpreadV) {
-      if constexpr (!kFreshVoff) {
-        if (rq.on) issue_v<D, QK, PV>(smem, wg, rq.kb, rq.buf, rq.base, N, voff);
-      } else {
-        uint32_t vo[TL::kSegPerWave];
-        fresh_voff(vo);
-        if (rq.on) issue_v<D, QK, PV>(smem, wg, rq.kb, rq.buf, rq.base, N, vo);
-      }
+      if (rq.on) issue_v<D, QK, PV>(smem, wg, rq.kb, rq.buf, rq.base, N, voff);
     }
     if constexpr (kFenced) {
       // The whole half-step in program order, fenced so that the scheduler
@@ -672,10 +649,11 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
           for (int r = 0; r < 16; ++r) s[ks][r] = (float)si[r];
         }
       }
-      if constexpr (DO_S && kScaleInM) {
+      if constexpr (DO_S && kScaleInX) {
         // t = code product * key scale, here rather than in the softmax
         // half-step, which bounds the 8-bit steps (the matrix half-step has
-        // the slack: its score products are half as many instructions)
+        // the slack: its score products are a quarter (fp8) or half (int8)
+        // as many instructions as bf16's)
         const float* skt = (const float*)(smem + TL::kOffSk + (jg % 3) * TL::kBytesSk);
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
@@ -706,13 +684,7 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
       }
     } else {
       if constexpr (ISSUE == 1) {
-        if constexpr (!kFreshVoff) {
-          if (rq.on) issue_k<D, QK, PV>(smem, wg, lane, rq.kb, rq.buf, rq.skbuf, rq.base, rq.sbase, N, voff);
-        } else {
-          uint32_t vo[TL::kSegPerWave];
-          fresh_voff(vo);
-          if (rq.on) issue_k<D, QK, PV>(smem, wg, lane, rq.kb, rq.buf, rq.skbuf, rq.base, rq.sbase, N, vo);
-        }
+        if (rq.on) issue_k<D, QK, PV>(smem, wg, lane, rq.kb, rq.buf, rq.skbuf, rq.base, rq.sbase, N, voff);
       }
       if constexpr (DO_PV) {
         const char* vt = (const char*)smem + TL::kOffV + ((jg - 1) & 1) * TL::kBytesV;
@@ -839,24 +811,6 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
   // ================= X_j: online softmax of block j
   auto half_x = [&](const int j) __attribute__((always_inline)) {
     const int kb = j * BC;
-    if constexpr (kScaleInX && !kScaleInM) {
-      // t = code product * key scale; the row's scale enters with the exp2
-      // argument (it is positive, so the row max is taken on t).  The
-      // products are fp32 here (int8: converted in the matrix step).
-      const float* skt = (const float*)(smem + TL::kOffSk + ((jg0 + j) % 3) * TL::kBytesSk);
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        const f32x4 a0 = *(const f32x4*)(skt + 32 * ks + 8 * g);
-        const f32x4 a1 = *(const f32x4*)(skt + 32 * ks + 8 * g + 4);
-        const f32x4 b0 = *(const f32x4*)(skt + 32 * ks + 16 + 8 * g);
-        const f32x4 b1 = *(const f32x4*)(skt + 32 * ks + 16 + 8 * g + 4);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float sk = r < 4 ? a0[r] : r < 8 ? a1[r - 4] : r < 12 ? b0[r - 8] : b1[r - 12];
-          s[ks][r] *= sk;  // products already fp32 (int8: converted in the matrix step)
-        }
-      }
-    }
     // causal diagonal and ragged tail: invisible keys score -inf.  The test
     // is per 32-key subtile first (uniform across the wave): subtiles wholly
     // visible are left alone, wholly invisible ones are set to -inf, and
