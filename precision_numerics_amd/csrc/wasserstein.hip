@@ -14,10 +14,12 @@
 //   histogram: workgroup g counts the digits of its contiguous chunk
 //   offsets:   per digit, the keys of smaller digits plus a scan of that
 //              digit's per-chunk counts
-//   scatter:   workgroup g walks its chunk in 256-element tiles; an element's
-//              rank among equal digits of its wave comes from eight ballots,
-//              the waves' counts are prefix-summed per digit in LDS, and the
-//              tile order keeps the sort stable
+//   scatter:   workgroup g walks its chunk in tiles of 4096 elements; an
+//              element's rank among equal digits of its wave comes from
+//              eight ballots, the runs' counts are prefix-summed per digit
+//              in LDS into a digit-sorted copy of the tile, which leaves as
+//              one contiguous run per digit; element order is kept
+//              throughout, so the sort is stable
 // The distances then come from one pass over both sorted key arrays with a
 // fixed element-to-thread map and fixed reduction trees (bitwise
 // reproducible).  Values are decoded exactly to fp64.  Off the attention hot
@@ -126,54 +128,113 @@ __global__ __launch_bounds__(kScanThreads) void digit_offsets(const uint32_t* co
   if (t < G) offsets[d * G + t] = base + part[t] - c;
 }
 
-// stable scatter of chunk g by the digit at `shift`
+// Stable scatter of chunk g by the digit at `shift`.  The chunk is walked in
+// tiles of kTileE * kThreads elements (element t + kThreads * s of a tile in
+// lane t, sub-tile s):
+//   1. every lane ranks its elements among the equal digits of its wave and
+//      sub-tile (eight ballots); each run's first lane records the run's
+//      length per (sub-tile, wave, digit)
+//   2. lane d turns the counts of digit d into starts in (sub-tile, wave)
+//      order, i.e. element order, and the tile's digit totals are scanned
+//      into the tile's digit-sorted layout
+//   3. every element goes to its place in that layout, in LDS
+//   4. lanes read the layout in order and write each element to the
+//      chunk's current global start of its digit plus its place in the
+//      digit's run: the elements of one digit leave as one contiguous run
+//      (consecutive lanes, consecutive addresses) instead of one key each
+// Within a digit, tiles, sub-tiles, waves and lanes follow element order,
+// so the sort stays stable.
+constexpr int kTileE = 16;
 template <typename K>
 __global__ __launch_bounds__(kThreads) void digit_scatter(const K* in, int64_t n, int64_t chunk,
                                                           int shift, const uint32_t* offsets,
                                                           K* out) {
-  __shared__ uint32_t base[256];          // global start of this chunk's digit-d run
-  __shared__ uint32_t wave_cnt[kWaves][256];
-  __shared__ uint32_t wave_pre[kWaves][256];
+  constexpr int kTile = kTileE * kThreads;
+  __shared__ uint32_t gbase[256];                   // global start of the chunk's digit-d run
+  __shared__ uint32_t tstart[256];                  // start of digit d in the tile layout
+  __shared__ uint32_t wsum[kWaves];
+  __shared__ uint16_t cnt[kTileE][kWaves][256];     // run lengths, then run starts
+  __shared__ K stage[kTile];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  base[tid] = offsets[(int64_t)tid * gridDim.x + blockIdx.x];
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) wave_cnt[w][tid] = 0;
-  __syncthreads();
+  gbase[tid] = offsets[(int64_t)tid * gridDim.x + blockIdx.x];
   const int64_t lo = (int64_t)blockIdx.x * chunk;
   const int64_t hi = lo + chunk < n ? lo + chunk : n;
   const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));  // lanes below this one
-  for (int64_t t0 = lo; t0 < hi; t0 += kThreads) {
-    const int64_t i = t0 + tid;
-    const bool valid = i < hi;
-    const K key = valid ? in[i] : (K)0;
-    const uint32_t dig = (uint32_t)(key >> shift) & 255u;
-    // lanes of this wave holding the same digit
-    uint64_t peers = __builtin_amdgcn_ballot_w64(valid);
+  for (int64_t t0 = lo; t0 < hi; t0 += kTile) {
+    K key[kTileE];
+    uint32_t dig[kTileE], rank[kTileE];
+    bool valid[kTileE];
 #pragma unroll
-    for (int b = 0; b < 8; ++b) {
-      const bool bit = (dig >> b) & 1u;
-      const uint64_t m = __builtin_amdgcn_ballot_w64(bit);
-      peers &= bit ? m : ~m;
+    for (int e = 0; e < kTileE; ++e) {
+      const int64_t i = t0 + (int64_t)e * kThreads + tid;
+      valid[e] = i < hi;
+      key[e] = valid[e] ? in[i] : (K)0;
     }
-    const uint32_t rank = (uint32_t)__builtin_popcountll(peers & lt);
-    if (valid && rank == 0) wave_cnt[wave][dig] = (uint32_t)__builtin_popcountll(peers);
+#pragma unroll
+    for (int e = 0; e < kTileE; ++e)
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) cnt[e][w][tid] = 0;
     __syncthreads();
-    {  // thread d: per-wave starts of digit d inside the chunk, then advance
-      uint32_t run = base[tid];
+#pragma unroll
+    for (int e = 0; e < kTileE; ++e) {
+      dig[e] = (uint32_t)(key[e] >> shift) & 255u;
+      uint64_t peers = __builtin_amdgcn_ballot_w64(valid[e]);
+#pragma unroll
+      for (int bit = 0; bit < 8; ++bit) {
+        const bool on = (dig[e] >> bit) & 1u;
+        const uint64_t m = __builtin_amdgcn_ballot_w64(on);
+        peers &= on ? m : ~m;
+      }
+      rank[e] = (uint32_t)__builtin_popcountll(peers & lt);
+      if (valid[e] && rank[e] == 0) cnt[e][wave][dig[e]] = (uint16_t)__builtin_popcountll(peers);
+    }
+    __syncthreads();
+    // lane d: starts of digit d's runs inside the digit, in element order,
+    // and the digit's total in this tile
+    uint32_t run = 0;
+#pragma unroll
+    for (int e = 0; e < kTileE; ++e)
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) {
-        wave_pre[w][tid] = run;
-        run += wave_cnt[w][tid];
-        wave_cnt[w][tid] = 0;
+        const uint32_t c = cnt[e][w][tid];
+        cnt[e][w][tid] = (uint16_t)run;
+        run += c;
       }
-      base[tid] = run;
+    // exclusive scan of the digit totals: in-wave, then across the waves
+    uint32_t inc = run;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint32_t v = __shfl_up(inc, off);
+      if (lane >= off) inc += v;
+    }
+    if (lane == 63) wsum[wave] = inc;
+    __syncthreads();
+    uint32_t before = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) before += w < wave ? wsum[w] : 0u;
+    const uint32_t my_start = before + inc - run;
+    tstart[tid] = my_start;
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < kTileE; ++e)
+      if (valid[e]) stage[tstart[dig[e]] + cnt[e][wave][dig[e]] + rank[e]] = key[e];
+    __syncthreads();
+    const int64_t m = hi - t0 < kTile ? hi - t0 : kTile;   // elements in this tile
+#pragma unroll
+    for (int e = 0; e < kTileE; ++e) {
+      const int p = e * kThreads + tid;
+      if (p < m) {
+        const K k = stage[p];
+        const uint32_t d = (uint32_t)(k >> shift) & 255u;
+        // the position lies in [0, n) by construction; the test keeps a
+        // counting error from ever writing outside the buffer
+        const uint32_t pos = gbase[d] + (uint32_t)p - tstart[d];
+        if ((int64_t)pos < n) out[pos] = k;
+      }
     }
     __syncthreads();
-    // the position lies in [0, n) by construction; the test keeps a
-    // counting error from ever writing outside the buffer
-    const uint32_t pos = wave_pre[wave][dig] + rank;
-    if (valid && (int64_t)pos < n) out[pos] = key;
-    __syncthreads();
+    gbase[tid] += run;
+    // the next tile's first barrier orders this update before its reads
   }
 }
 
