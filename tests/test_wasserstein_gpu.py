@@ -63,7 +63,7 @@ def _check(pna, a_np, b_np, what):
     return got
 
 
-@pytest.mark.parametrize("n", [1, 2, 63, 257, 70001, (1 << 20) + 3])
+@pytest.mark.parametrize("n", [1, 2, 63, 257, 4096, 70001, 81920, (1 << 20) + 3])
 @pytest.mark.parametrize("dts", [("bf16", "f64"), ("f32", "f64"), ("bf16", "bf16"),
                                  ("f32", "bf16"), ("f64", "f64")])
 def test_matches_oracle(lib, n, dts):
