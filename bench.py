@@ -67,8 +67,8 @@ TRAFFIC_SOURCES = ("precision_numerics_amd/csrc/flash_fwd.hip",
                    "precision_numerics_amd/csrc/lds_dma.hpp")
 TRAFFIC = {
     "workload": "c3",
-    "sources_sha256": "7b68e17d1584ff10c166519336dcd55ca6311a733b545792ad3b5ec9e4884e06",
-    "fetch_kib": 306694.0, "fetch_scale": 2.0,
+    "sources_sha256": "4735a4a0c70ab699fe63c710d0e0c0944a8aebf1d9eab347c979b65a56ba9815",
+    "fetch_kib": 305044.0, "fetch_scale": 2.0,
     "write_kib": 131072.0, "write_scale": 1.0,
 }
 

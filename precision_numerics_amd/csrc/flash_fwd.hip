@@ -105,13 +105,12 @@ template <int D, int QK, int PV> struct Tile {
   static constexpr int kSegVPerWave = (kSegV + kIssuers - 1) / kIssuers;
   static constexpr int kSegPerWave = kSegKPerWave > kSegVPerWave ? kSegKPerWave : kSegVPerWave;
   static constexpr int kBytesSk = kScaledQK<QK> ? kBC * 4 : 0;
-  // [K buf0][K buf1][V buf0][V buf1][sk buf0][sk buf1][sk buf2].  The fp8
-  // key scales of block j are read in the softmax half-step X_j, which
-  // group 1 runs while group 0 already loads block j + 2: they take three
-  // buffers (int8 reads them earlier, in M_j).
+  // [K buf0][K buf1][V buf0][V buf1][sk buf0][sk buf1].  The key scales of
+  // block j are read at the end of each group's M_j; those of block j + 2
+  // load in group 0's M_{j+1}, after group 1's M_j.
   static constexpr int kOffV = 2 * kBytesK;
   static constexpr int kOffSk = kOffV + 2 * kBytesV;
-  static constexpr int kLds = kOffSk + 3 * kBytesSk;
+  static constexpr int kLds = kOffSk + 2 * kBytesSk;
   static_assert(kBytesK % 1024 == 0 && kBytesV % 1024 == 0, "tiles must be whole segments");
 };
 
@@ -581,7 +580,7 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
         if (i < NPV) {
           oacc[i % DT] = mfma_bf16(join_bf16x8(vlo[i], vhi[i]), pb[i / DT], oacc[i % DT]);
         } else {
-          // 8-bit Q/K: raw int32 (or fp32 fp8) products; the softmax
+          // 8-bit Q/K: raw int32 (or fp32 fp8) products; the end of the
           // half-step applies the key scales
           const int t = i - NPV;
           if constexpr (QK == QK_BF16)
@@ -654,7 +653,7 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
         // half-step, which bounds the 8-bit steps (the matrix half-step has
         // the slack: its score products are a quarter (fp8) or half (int8)
         // as many instructions as bf16's)
-        const float* skt = (const float*)(smem + TL::kOffSk + (jg % 3) * TL::kBytesSk);
+        const float* skt = (const float*)(smem + TL::kOffSk + (jg & 1) * TL::kBytesSk);
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
           const f32x4 a0 = *(const f32x4*)(skt + 32 * ks + 8 * g);
@@ -755,7 +754,7 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) s[ks][r] = acc[ks][r];  // raw q.k; scaled inside exp2
         } else if constexpr (QK == QK_I8) {
-          const float* skt = (const float*)(smem + TL::kOffSk + (jg % 3) * TL::kBytesSk);
+          const float* skt = (const float*)(smem + TL::kOffSk + (jg & 1) * TL::kBytesSk);
 #pragma unroll
           for (int ks = 0; ks < NKS; ++ks) {
             const char* krow = kt + ks * 32 * TL::kStrK + k_lane + 16 * g;
@@ -781,7 +780,7 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
         } else if constexpr (QK == QK_F8) {
           // E4M3 codes in the int8 layout: two fp8 products per 32-byte
           // chunk of the row, then the per-row scales as for int8
-          const float* skt = (const float*)(smem + TL::kOffSk + (jg % 3) * TL::kBytesSk);
+          const float* skt = (const float*)(smem + TL::kOffSk + (jg & 1) * TL::kBytesSk);
 #pragma unroll
           for (int ks = 0; ks < NKS; ++ks) {
             const char* krow = kt + ks * 32 * TL::kStrK + k_lane + 16 * g;
@@ -1037,7 +1036,7 @@ __global__ __launch_bounds__(kThreads) void flash_fwd_kernel(FlashParams p) {
     const int b = same ? cur.bh : nxt.bh;
     return Prefetch{head_ptr(p.k, b, sizeof(QT)),
                     kScaledQK<QK> ? (const void*)(p.k_scale + (int64_t)b * N) : nullptr,
-                    same ? (j + 1) * BC : 0, (jg0 + j + 1) & 1, (jg0 + j + 1) % 3,
+                    same ? (j + 1) * BC : 0, (jg0 + j + 1) & 1, (jg0 + j + 1) & 1,
                     same || nxt.valid};
   };
   // the V block of local block j of the current tile
