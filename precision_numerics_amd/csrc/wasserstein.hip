@@ -98,17 +98,34 @@ __global__ __launch_bounds__(kThreads) void digit_histogram(const K* keys, int64
 }
 
 // offsets[d * G + g] = number of keys with a smaller digit, plus those with
-// digit d in chunks before g: workgroup d sums the counts of all smaller
-// digits and scans its own G <= 1024 counts (one per thread).  Integer sums:
-// exact in any order.
+// digit d in chunks before g.  digit_totals: workgroup d sums its digit's G
+// <= 1024 counts; digit_offsets: workgroup d adds the totals of the smaller
+// digits and scans its own counts (one per thread).  Integer sums: exact in
+// any order.
 constexpr int kScanThreads = 1024;
+__global__ __launch_bounds__(kScanThreads) void digit_totals(const uint32_t* counts, int G,
+                                                             uint32_t* totals) {
+  __shared__ uint32_t red[kScanThreads / 64];
+  const int d = blockIdx.x, t = threadIdx.x;
+  uint32_t c = t < G ? counts[d * G + t] : 0u;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) c += __shfl_xor(c, off);
+  if ((t & 63) == 0) red[t >> 6] = c;
+  __syncthreads();
+  if (t == 0) {
+    uint32_t sum = 0;
+#pragma unroll
+    for (int w = 0; w < kScanThreads / 64; ++w) sum += red[w];
+    totals[d] = sum;
+  }
+}
 __global__ __launch_bounds__(kScanThreads) void digit_offsets(const uint32_t* counts, int G,
+                                                              const uint32_t* totals,
                                                               uint32_t* offsets) {
   __shared__ uint32_t part[kScanThreads];
   __shared__ uint32_t red[kScanThreads / 64];
   const int d = blockIdx.x, t = threadIdx.x;
-  uint32_t below = 0;
-  for (int i = t; i < d * G; i += kScanThreads) below += counts[i];
+  uint32_t below = t < d ? totals[t] : 0u;  // d < 256 <= kScanThreads
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) below += __shfl_xor(below, off);
   if ((t & 63) == 0) red[t >> 6] = below;
@@ -307,7 +324,7 @@ size_t key_bytes(int dtype) { return dtype == kBF16 ? 2 : (dtype == kF32 ? 4 : 8
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Layout {
-  size_t a0, a1, b0, b1, counts, offsets, bad, parts, rec, total;
+  size_t a0, a1, b0, b1, counts, totals, offsets, bad, parts, rec, total;
 };
 
 Layout layout(int64_t n, int a_dtype, int b_dtype) {
@@ -324,6 +341,7 @@ Layout layout(int64_t n, int a_dtype, int b_dtype) {
   l.b0 = take((size_t)n * key_bytes(b_dtype));
   l.b1 = take((size_t)n * key_bytes(b_dtype));
   l.counts = take(256 * G * 4);
+  l.totals = take(256 * 4);
   l.offsets = take(256 * G * 4);
   l.bad = take(2 * G * 4);
   l.parts = take(G * sizeof(WPartial));
@@ -340,6 +358,7 @@ hipError_t sort_keys(const void* x, int64_t n, char* scratch, size_t off0, size_
   const int64_t chunk = (n + G - 1) / G;
   K* buf[2] = {(K*)(scratch + off0), (K*)(scratch + off1)};
   uint32_t* counts = (uint32_t*)(scratch + l.counts);
+  uint32_t* totals = (uint32_t*)(scratch + l.totals);
   uint32_t* offsets = (uint32_t*)(scratch + l.offsets);
   hipLaunchKernelGGL((make_keys<K>), dim3(G), dim3(kThreads), 0, st, (const K*)x, n, chunk,
                      buf[0], bad);
@@ -349,7 +368,8 @@ hipError_t sort_keys(const void* x, int64_t n, char* scratch, size_t off0, size_
   for (int shift = 0; shift < (int)(8 * sizeof(K)); shift += 8) {
     hipLaunchKernelGGL((digit_histogram<K>), dim3(G), dim3(kThreads), 0, st, buf[cur], n, chunk,
                        shift, counts);
-    hipLaunchKernelGGL(digit_offsets, dim3(256), dim3(kScanThreads), 0, st, counts, G, offsets);
+    hipLaunchKernelGGL(digit_totals, dim3(256), dim3(kScanThreads), 0, st, counts, G, totals);
+    hipLaunchKernelGGL(digit_offsets, dim3(256), dim3(kScanThreads), 0, st, counts, G, totals, offsets);
     hipLaunchKernelGGL((digit_scatter<K>), dim3(G), dim3(kThreads), 0, st, buf[cur], n, chunk,
                        shift, offsets, buf[cur ^ 1]);
     e = hipGetLastError();
