@@ -254,6 +254,39 @@ def test_deviation_matches_oracle(lib, n, dtype):
     assert again == got                                   # bitwise reproducible
 
 
+
+@pytest.mark.parametrize("n", [1, 4095, 70001])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_deviation_unaligned_views(lib, n, dtype):
+    """Operands one element past a 16-byte boundary take the element-wise
+    first pass: same oracle agreement, and the same result as aligned copies
+    of the same values."""
+    import precision_numerics_amd as pna
+    rng = np.random.default_rng(100 + n)
+    ref = rng.standard_normal(n + 1)
+    test32 = (ref + rng.standard_normal(n + 1) * 1e-3).astype(np.float32)
+    if n >= 3:
+        test32[1 + n // 2] = np.nan
+    if dtype == "bf16":
+        bits = synth.f32_to_bf16_bits(test32)
+        t_all = torch_bf16(bits)
+        test = synth.bf16_bits_to_f32(bits).astype(np.float64)[1:]
+    else:
+        t_all = torch.from_numpy(test32).cuda()
+        test = test32.astype(np.float64)[1:]
+    r_all = torch.from_numpy(ref).cuda()
+    t_view, r_view = t_all[1:], r_all[1:]          # 2 or 4 and 8 bytes past the allocation start
+    assert t_view.data_ptr() % 16 != 0 and r_view.data_ptr() % 16 != 0
+    got = pna.attn_deviation(t_view, r_view)
+    want = oracle.deviation(test, ref[1:])
+    assert got["n"] == want["n"] and got["n_nonfinite"] == want["n_nonfinite"]
+    assert got["argmax"] == want["argmax"] and got["max_abs"] == want["max_abs"]
+    for key in ("mean_abs", "mean_signed", "rms", "rel_normwise"):
+        assert abs(got[key] - want[key]) <= 1e-12 * max(1e-300, abs(want[key])) + 1e-300, key
+    aligned = pna.attn_deviation(t_view.clone(), r_view.clone())
+    assert aligned["argmax"] == got["argmax"] and aligned["max_abs"] == got["max_abs"]
+    assert aligned["n_nonfinite"] == got["n_nonfinite"]
+
 # ---------------------------------------------------------------------------
 # the five workloads at full size (bench launch configuration)
 # ---------------------------------------------------------------------------
